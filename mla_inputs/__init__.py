@@ -1,0 +1,21 @@
+"""Seeded synthetic inputs for MLA absorbed decode.
+
+This package only draws random numbers, rounds them to the storage formats
+(bf16, fp32, OCP FP8 E4M3 with a per-token scale) and lays the cached rows
+out in memory (contiguous or paged in 64-token blocks).  It contains none of
+the attention arithmetic: no RoPE, no projection, no softmax.  Both the CPU
+oracle and the GPU path consume what it produces.
+"""
+
+from .configs import BLOCK_TOKENS, CONFIGS, HEADLINE, MLAConfig, scaled
+from .generate import MLAInputs, Pool
+
+__all__ = [
+    "BLOCK_TOKENS",
+    "CONFIGS",
+    "HEADLINE",
+    "MLAConfig",
+    "MLAInputs",
+    "Pool",
+    "scaled",
+]
