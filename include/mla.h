@@ -1,0 +1,203 @@
+/*
+ * mla.h -- C ABI of the MI355X (gfx950) MLA absorbed-decode library.
+ *
+ * One decode step of DeepSeek-style Multi-Head Latent Attention with matrix
+ * absorption, as four calls on one HIP stream:
+ *
+ *   mla_absorb_q     q_abs = [ W_UK^T q_nope ; RoPE(q_rope) ]      per head
+ *   mla_decode_attn  split-K attention of every head against the shared
+ *                    cached rows [c_kv ; k_rope] -> partial o_lat + lse
+ *   mla_combine      log-sum-exp merge of the partials -> o_lat
+ *   mla_out_proj     o = W_UV o_lat                                per head
+ *
+ * Uncompressed per-head keys and values are never written to memory.
+ *
+ * Pages cited (title, section):
+ *   [ARCH] "Model Architecture Driving Inference Systems: From MHA/GQA to
+ *          DeepSeek MLA Matrix Absorption and Memory Minimalism"
+ *   [MATH] "Multi-Head Latent Attention (MLA): Mathematical Foundations,
+ *          Low-Rank KV Compression, Decoupled Rotary Positional Embeddings,
+ *          and Inference Matrix Absorption"
+ *
+ * Conventions shared by every call:
+ *   - Tensor arguments are DEVICE pointers, row-major, innermost dimension
+ *     contiguous, 16-byte aligned.  `dims` and the scalars are read on the
+ *     host.  The caller owns all memory; no call allocates or frees.
+ *   - Every call only validates its host arguments and enqueues kernels on
+ *     `stream` (a hipStream_t; NULL = the null stream).  Nothing is
+ *     synchronised.  Argument errors are reported before anything is
+ *     enqueued, and then nothing is enqueued.
+ *   - Device-side contents (seq_lens, positions, block_table) are trusted:
+ *     0 <= seq_lens[b] <= max_seq_len, block ids inside the pool.  Violations
+ *     are undefined behaviour.
+ *   - No call keeps state between calls; calls are reentrant.
+ *   - Return value: MLA_OK or one of the error codes below.
+ */
+#ifndef MLA_H
+#define MLA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  MLA_OK = 0,
+  MLA_ERR_INVALID_ARG = 1, /* NULL pointer, bad size, misalignment, bad enum  */
+  MLA_ERR_UNSUPPORTED = 2, /* valid but not built (dtype mix, width limits)   */
+  MLA_ERR_WORKSPACE = 3,   /* workspace pointers missing                     */
+  MLA_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed     */
+};
+
+/* Element types. */
+enum {
+  MLA_F32 = 0,
+  MLA_BF16 = 1,
+  MLA_FP8_E4M3 = 2 /* OCP E4M3 "fn": bias 7, max 448, no inf; cache only */
+};
+
+/* Flags in mla_dims_t.flags. */
+enum {
+  MLA_FLAG_GENERIC = 1 /* force the plain SIMT kernels instead of MFMA ones */
+};
+
+/* Cached tokens are processed, and split-K work is divided, in tiles of
+ * this many tokens; a paged cache must use blocks of this many rows
+ * ([ARCH] 4.1: page blocks of 64). */
+#define MLA_TILE_TOKENS 64
+
+typedef struct mla_dims {
+  int32_t batch;    /* B, sequences (0 = nothing to do)                     */
+  int32_t q_len;    /* Lq, query tokens per sequence (>= 1)                  */
+  int32_t heads;    /* H, attention heads                                    */
+  int32_t d_nope;   /* per-head content query/key width (DeepSeek-V3: 128)   */
+  int32_t d_rope;   /* decoupled RoPE width, even (64)                       */
+  int32_t d_latent; /* latent width d_c (512)                                */
+  int32_t d_v;      /* per-head value width (128)                            */
+  int32_t q_dtype;  /* MLA_F32 or MLA_BF16: q_nope, q_rope, w_uk, w_uv,
+                       q_abs, o_lat, o                                       */
+  int32_t kv_dtype; /* MLA_F32 (with q F32), MLA_BF16 or MLA_FP8_E4M3
+                       (with q BF16): the cache                              */
+  int32_t flags;    /* MLA_FLAG_* */
+} mla_dims_t;
+
+/*
+ * mla_absorb_q -- key absorption and query RoPE.
+ *
+ * [ARCH] 3.1: the content score q^C . (W_UK,i c_j) is regrouped as
+ * (W_UK,i^T q^C) . c_j, so each head's query is mapped once per step into the
+ * latent space and scored against the raw cached latents.  [ARCH] 2.3 /
+ * [MATH] "The Decoupled RoPE Solution": the positional part of the query is
+ * rotated by RoPE; [MATH] reference module (apply_rope): consecutive pairs
+ * (x[2k], x[2k+1]) turn by angle pos * rope_base^(-2k/d_rope).
+ *
+ *   q_nope    [B, Lq, H, d_nope]          q_dtype
+ *   q_rope    [B, Lq, H, d_rope]          q_dtype, before rotation
+ *   positions [B, Lq]                     int32, token position of each query
+ *   rope_base                             e.g. 10000
+ *   w_uk      [H, d_nope, d_latent]       q_dtype, W_UK,i = w_uk[i] (d_nope x d_latent)
+ *   q_abs     [B, Lq, H, d_latent+d_rope] q_dtype, output:
+ *             q_abs[..., :d_latent] = w_uk[h]^T q_nope   (fp32 accumulate)
+ *             q_abs[..., d_latent:] = RoPE(q_rope, pos)  (angle in fp64)
+ */
+int mla_absorb_q(const mla_dims_t* dims, const void* q_nope, const void* q_rope,
+                 const int32_t* positions, float rope_base, const void* w_uk,
+                 void* q_abs, void* stream);
+
+/*
+ * mla_decode_attn -- split-K attention over the shared latent cache.
+ *
+ * [ARCH] 3.1 score: S_t = (q~ . c_t + q^R . k^R_t) * softmax_scale with the
+ * absorbed query q~ and the decoupled key k^R shared by all heads (2.3);
+ * softmax over the cached tokens; [ARCH] 3.2: the weights multiply the raw
+ * latents, giving the 512-wide latent output sum_t P_t c_t.
+ *
+ * Cache rows.  Token t of sequence b lives in row
+ *     r = block_table ? block_table[b*max_blocks_per_seq + t/64]*64 + t%64
+ *                     : b*max_seq_len + t
+ * with its latent at latent_cache + r*kv_row_stride (d_latent elements) and
+ * its post-RoPE key at rope_cache + r*kv_row_stride (d_rope elements).  The
+ * fused layout is kv_row_stride = d_latent + d_rope and
+ * rope_cache = latent_cache + d_latent.  For MLA_FP8_E4M3 the stored value
+ * is code * kv_scale[r] (one fp32 scale per token).
+ *
+ *   q_abs        [B, Lq, H, d_latent+d_rope] q_dtype (output of mla_absorb_q)
+ *   seq_lens     [B] int32, cached tokens per sequence
+ *   block_table  [B, max_blocks_per_seq] int32, or NULL for contiguous rows
+ *   block_size   must be MLA_TILE_TOKENS when block_table != NULL
+ *   max_seq_len  bound on seq_lens; row pitch of the contiguous layout
+ *   causal       0: every query sees all seq_lens[b] tokens; 1: query i sees
+ *                tokens t <= seq_lens[b] - Lq + i
+ *   num_splits   G >= 1 work units.  The 64-token tiles of all sequences,
+ *                taken in order, are divided evenly: unit u covers global
+ *                tiles [floor(u*T/G), floor((u+1)*T/G)) where T is the total
+ *                tile count.  Each unit writes one partial per sequence it
+ *                touches, into slot u + b.
+ *   o_part       [G + B - 1, Lq*H, d_latent] fp32 workspace: normalised
+ *                partial latent outputs (row index i*H + h)
+ *   lse_part     [G + B - 1, Lq*H] fp32 workspace: natural-log LSE of each
+ *                partial (-inf when the partial saw no token)
+ */
+int mla_decode_attn(const mla_dims_t* dims, const void* q_abs, const void* latent_cache,
+                    const void* rope_cache, int64_t kv_row_stride, const float* kv_scale,
+                    const int32_t* seq_lens, const int32_t* block_table,
+                    int32_t max_blocks_per_seq, int32_t block_size, int32_t max_seq_len,
+                    int32_t causal, float softmax_scale, int32_t num_splits, float* o_part,
+                    float* lse_part, void* stream);
+
+/*
+ * mla_combine -- merge the split-K partials of mla_decode_attn.
+ *
+ * For each sequence b and row (i, h), with the units that touched b:
+ *   lse = log sum_u exp(lse_u);  o_lat = sum_u exp(lse_u - lse) o_u.
+ * This is the softmax over all of b's tokens ([MATH] "Value Output Matrix
+ * Absorption": softmax weights applied to the cached latents).
+ *
+ *   num_splits, seq_lens, o_part, lse_part: as passed to mla_decode_attn
+ *   o_lat   [B, Lq, H, d_latent] q_dtype, output (0 where no token was seen)
+ *   lse_out [B, Lq, H] fp32 natural-log LSE, output; may be NULL
+ */
+int mla_combine(const mla_dims_t* dims, int32_t num_splits, const int32_t* seq_lens,
+                const float* o_part, const float* lse_part, void* o_lat, float* lse_out,
+                void* stream);
+
+/*
+ * mla_out_proj -- value up-projection of the latent output.
+ *
+ * [ARCH] 3.2: o_i = sum_j P_ij W_UV,i c_j = W_UV,i (sum_j P_ij c_j).
+ *
+ *   o_lat [B, Lq, H, d_latent] q_dtype
+ *   w_uv  [H, d_v, d_latent]   q_dtype, W_UV,i = w_uv[i] (d_v x d_latent)
+ *   o     [B, Lq, H, d_v]      q_dtype, output (fp32 accumulate)
+ */
+int mla_out_proj(const mla_dims_t* dims, const void* o_lat, const void* w_uv, void* o,
+                 void* stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* mla_status_string(int status);
+
+/* Element counts of the two split-K workspaces for `num_splits` units. */
+int mla_workspace_elems(const mla_dims_t* dims, int32_t num_splits, int64_t* o_part_elems,
+                        int64_t* lse_part_elems);
+
+/* A good num_splits for `device`: one work unit per compute unit and row
+ * group of 128 query rows.  Host-only query of device properties. */
+int mla_num_splits_hint(const mla_dims_t* dims, int32_t device, int32_t* num_splits);
+
+/*
+ * mla_split_plan -- host-side view of the split-K division (no GPU use).
+ *
+ * For host-resident seq_lens[B], writes for every sequence b the first and
+ * last unit that touch it (-1, -1 when seq_lens[b] == 0) and its first
+ * global tile.  Units first_unit[b]..last_unit[b] hold b's partials in slots
+ * u + b.  Useful to size and inspect the workspaces.
+ */
+int mla_split_plan(int32_t batch, const int32_t* seq_lens_host, int32_t num_splits,
+                   int32_t* first_unit, int32_t* last_unit, int64_t* first_tile);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_H */

@@ -1,0 +1,52 @@
+// Kernel launchers of the MLA decode library (internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/mla.h"
+
+namespace mla {
+
+struct DecodeArgs {
+  const void* q_abs;
+  const void* latent;
+  const void* rope;
+  int64_t row_stride;      // elements between consecutive cache rows
+  const float* kv_scale;   // fp8 per-row scale, else nullptr
+  const int32_t* seq_lens;
+  const int32_t* block_table;
+  int mbps;                // max_blocks_per_seq
+  int max_seq_len;
+  int batch, q_len, heads, d_c, d_r;
+  int causal;
+  float softmax_scale;
+  int num_splits;
+  float* o_part;
+  float* lse_part;
+};
+
+hipError_t launch_absorb_generic(const mla_dims_t& d, const void* q_nope, const void* q_rope,
+                                 const int32_t* positions, float rope_base, const void* w_uk,
+                                 void* q_abs, hipStream_t s);
+bool generic_decode_supports(const mla_dims_t& d);
+hipError_t launch_decode_generic(const mla_dims_t& d, const DecodeArgs& a, hipStream_t s);
+hipError_t launch_out_proj_generic(const mla_dims_t& d, const void* o_lat, const void* w_uv,
+                                   void* o, hipStream_t s);
+hipError_t launch_combine(const mla_dims_t& d, int num_splits, const int32_t* seq_lens,
+                          const float* o_part, const float* lse_part, void* o_lat,
+                          float* lse_out, hipStream_t s);
+
+// MFMA kernels (bf16 queries and weights, gfx950).
+bool mfma_absorb_supports(const mla_dims_t& d);
+hipError_t launch_absorb_mfma(const mla_dims_t& d, const void* q_nope, const void* q_rope,
+                              const int32_t* positions, float rope_base, const void* w_uk,
+                              void* q_abs, hipStream_t s);
+bool mfma_decode_supports(const mla_dims_t& d, int64_t row_stride, const void* latent,
+                          const void* rope);
+hipError_t launch_decode_mfma(const mla_dims_t& d, const DecodeArgs& a, hipStream_t s);
+bool mfma_out_proj_supports(const mla_dims_t& d);
+hipError_t launch_out_proj_mfma(const mla_dims_t& d, const void* o_lat, const void* w_uv,
+                                void* o, hipStream_t s);
+
+}  // namespace mla

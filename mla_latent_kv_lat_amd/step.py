@@ -1,0 +1,47 @@
+"""One decode step: buffers and the four library calls in order.
+
+Argument marshalling only: torch allocates the caller-owned outputs and
+split-K workspaces once; ``run`` enqueues mla_absorb_q, mla_decode_attn,
+mla_combine and mla_out_proj on the current stream.
+"""
+
+from __future__ import annotations
+
+import torch
+
+from . import binding as _b
+
+TORCH_DTYPE = {_b.F32: torch.float32, _b.BF16: torch.bfloat16}
+
+
+class DecodeStep:
+    def __init__(self, d: _b.MLADims, *, num_splits: int | None = None, device="cuda"):
+        self.d = d
+        self.device = torch.device(device)
+        self.num_splits = int(num_splits) if num_splits else _b.mla_num_splits_hint(
+            d, self.device.index or 0)
+        qt = TORCH_DTYPE[d.q_dtype]
+        B, Lq, H = d.batch, d.q_len, d.heads
+        W = d.d_latent + d.d_rope
+        n_o, n_l = _b.mla_workspace_elems(d, self.num_splits)
+        kw = dict(device=self.device)
+        self.q_abs = torch.empty((B, Lq, H, W), dtype=qt, **kw)
+        self.o_part = torch.empty(max(n_o, 1), dtype=torch.float32, **kw)
+        self.lse_part = torch.empty(max(n_l, 1), dtype=torch.float32, **kw)
+        self.o_lat = torch.empty((B, Lq, H, d.d_latent), dtype=qt, **kw)
+        self.lse = torch.empty((B, Lq, H), dtype=torch.float32, **kw)
+        self.o = torch.empty((B, Lq, H, d.d_v), dtype=qt, **kw)
+
+    def run(self, *, q_nope, q_rope, positions, w_uk, w_uv, latent, rope, kv_row_stride,
+            kv_scale, seq_lens, block_table, max_blocks_per_seq, max_seq_len, causal,
+            softmax_scale, rope_base=10000.0, stream=None):
+        d = self.d
+        _b.mla_absorb_q(d, q_nope, q_rope, positions, rope_base, w_uk, self.q_abs, stream)
+        _b.mla_decode_attn(d, self.q_abs, latent, rope, kv_row_stride, kv_scale, seq_lens,
+                           block_table, max_blocks_per_seq, _b.TILE_TOKENS, max_seq_len,
+                           causal, softmax_scale, self.num_splits, self.o_part, self.lse_part,
+                           stream)
+        _b.mla_combine(d, self.num_splits, seq_lens, self.o_part, self.lse_part, self.o_lat,
+                       self.lse, stream)
+        _b.mla_out_proj(d, self.o_lat, w_uv, self.o, stream)
+        return self.o

@@ -1,0 +1,136 @@
+"""C ABI checks that need no GPU: the library loads, every declared entry
+point is exported, host validation rejects bad arguments before any HIP
+call, and the split-K division is a partition with distinct slots."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import mla_latent_kv_lat_amd as mla
+from mla_latent_kv_lat_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    txt = open(os.path.join(ROOT, "include", "mla.h")).read()
+    return sorted(set(re.findall(r"^(?:int|const char\*)\s+(mla_\w+)\(", txt, re.M)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared()
+    assert {"mla_absorb_q", "mla_decode_attn", "mla_combine", "mla_out_proj"} <= set(names)
+    lib = binding.library()
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    lib = binding.library()
+    for code in range(5):
+        assert lib.mla_status_string(code).decode().startswith("MLA_")
+
+
+DSV3 = dict(batch=2, q_len=1, heads=128, d_nope=128, d_rope=64, d_latent=512, d_v=128,
+            q_dtype=mla.BF16, kv_dtype=mla.BF16)
+
+
+def _d(**kw):
+    a = dict(DSV3)
+    a.update(kw)
+    return mla.dims(**a)
+
+
+def _decode(d, **kw):
+    a = dict(q_abs=16, latent_cache=16, rope_cache=16 + 1024, kv_row_stride=576, kv_scale=None,
+             seq_lens=16, block_table=None, max_blocks_per_seq=0, block_size=64, max_seq_len=64,
+             causal=0, softmax_scale=0.07, num_splits=4, o_part=16, lse_part=16)
+    a.update(kw)
+    return binding._lib.mla_decode_attn(ctypes.byref(d), a["q_abs"], a["latent_cache"],
+                                        a["rope_cache"], a["kv_row_stride"], a["kv_scale"],
+                                        a["seq_lens"], a["block_table"], a["max_blocks_per_seq"],
+                                        a["block_size"], a["max_seq_len"], a["causal"],
+                                        a["softmax_scale"], a["num_splits"], a["o_part"],
+                                        a["lse_part"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q_len=0), 1), (dict(heads=0), 1), (dict(d_rope=63), 1), (dict(d_latent=500), 1),
+    (dict(q_dtype=7), 1), (dict(kv_dtype=9), 1), (dict(flags=8), 1),
+    (dict(q_dtype=mla.F32), 2), (dict(kv_dtype=mla.F32), 2),
+])
+def test_bad_dims_rejected(kw, status):
+    assert _decode(_d(**kw)) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q_abs=None), 1), (dict(seq_lens=None), 1), (dict(o_part=None), 3),
+    (dict(lse_part=None), 3), (dict(q_abs=8), 1), (dict(kv_row_stride=100), 1),
+    (dict(num_splits=0), 1), (dict(num_splits=70000), 1), (dict(causal=2), 1),
+    (dict(softmax_scale=0.0), 1), (dict(softmax_scale=float("nan")), 1),
+    (dict(max_seq_len=0), 1), (dict(kv_scale=16), 1),
+    (dict(block_table=16, block_size=32, max_blocks_per_seq=1), 1),
+    (dict(block_table=16, block_size=64, max_blocks_per_seq=1, max_seq_len=65), 1),
+])
+def test_bad_decode_args_rejected(kw, status):
+    assert _decode(_d(), **kw) == status
+
+
+def test_fp8_needs_scale():
+    assert _decode(_d(kv_dtype=mla.FP8_E4M3)) == 1
+
+
+def test_empty_batch_is_a_noop():
+    assert _decode(_d(batch=0)) == 0
+    d = _d(batch=0)
+    assert binding._lib.mla_combine(ctypes.byref(d), 4, 16, 16, 16, 16, None, None) == 0
+    assert binding._lib.mla_out_proj(ctypes.byref(d), 16, 16, 16, None) == 0
+    assert binding._lib.mla_absorb_q(ctypes.byref(d), 16, 16, 16, 10000.0, 16, 16, None) == 0
+
+
+def test_other_entry_points_validate():
+    d = _d()
+    lib = binding._lib
+    assert lib.mla_absorb_q(ctypes.byref(d), None, 16, 16, 10000.0, 16, 16, None) == 1
+    assert lib.mla_absorb_q(ctypes.byref(d), 16, 16, 16, -1.0, 16, 16, None) == 1
+    assert lib.mla_combine(ctypes.byref(d), 4, 16, None, 16, 16, None, None) == 3
+    assert lib.mla_combine(ctypes.byref(d), 0, 16, 16, 16, 16, None, None) == 1
+    assert lib.mla_out_proj(ctypes.byref(d), 16, None, 16, None) == 1
+    with pytest.raises(mla.MLAError):
+        mla.mla_out_proj(d, 16, None, 16, stream=0)
+
+
+def test_workspace_elems():
+    d = _d(batch=64, q_len=2)
+    o, l = mla.mla_workspace_elems(d, 128)
+    assert l == (128 + 64 - 1) * 256 and o == l * 512
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_split_plan_is_a_partition(seed):
+    rng = np.random.default_rng(seed)
+    B = int(rng.integers(1, 40))
+    lens = rng.integers(0, 2000, size=B) * (rng.random(B) > 0.2)
+    G = int(rng.integers(1, 300))
+    fu, lu, ft = mla.mla_split_plan(lens, G)
+    tiles = -(-lens // 64)
+    T = int(tiles.sum())
+    begin = [u * T // G for u in range(G + 1)]
+    assert np.array_equal(ft, np.concatenate([[0], np.cumsum(tiles)[:-1]]))
+    slots = set()
+    for b in range(B):
+        if tiles[b] == 0:
+            assert fu[b] == -1 and lu[b] == -1
+            continue
+        lo, hi = ft[b], ft[b] + tiles[b]
+        touching = [u for u in range(G) if begin[u] < begin[u + 1] and begin[u] < hi and begin[u + 1] > lo]
+        assert touching[0] == fu[b] and touching[-1] == lu[b]
+        covered = sum(min(hi, begin[u + 1]) - max(lo, begin[u]) for u in touching)
+        assert covered == tiles[b]
+        for u in touching:
+            assert u + b not in slots
+            slots.add(u + b)
+    assert all(s < G + B - 1 for s in slots)

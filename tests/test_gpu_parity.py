@@ -1,0 +1,130 @@
+"""GPU parity: the HIP path through the C ABI against the float64 oracle.
+
+Each case runs the four calls of one decode step on seeded inputs and
+compares every stage with the oracle: q_abs with the absorbed query and the
+rotated RoPE query, o_lat and lse with the absorbed intermediates, and o
+with the non-absorbed definition.  Gates (row-normwise max relative error):
+1e-5 fp32, 2e-2 bf16, 5e-2 fp8 cache.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import mla_latent_kv_lat_amd as mla
+from mla_inputs import CONFIGS, MLAInputs, scaled
+from mla_inputs.device import to_device
+from oracle import mla_absorbed, mla_decode
+from tests._metrics import row_rel_err, tol_for
+
+pytestmark = pytest.mark.gpu
+
+DT = {"f32": mla.F32, "bf16": mla.BF16, "fp8": mla.FP8_E4M3}
+
+
+def _np(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def run_gpu(inp, *, flags=0, num_splits=None, dev=None):
+    c = inp.cfg
+    dev = dev or to_device(inp)
+    d = mla.dims(c.batch, c.q_len, c.heads, c.d_nope, c.d_rope, c.d_latent, c.d_v,
+                 DT[c.q_dtype], DT[c.kv_dtype], flags)
+    step = mla.DecodeStep(d, num_splits=num_splits)
+    step.run(q_nope=dev.q_nope, q_rope=dev.q_rope, positions=dev.positions, w_uk=dev.w_uk,
+             w_uv=dev.w_uv, latent=dev.latent, rope=dev.rope, kv_row_stride=dev.kv_row_stride,
+             kv_scale=dev.kv_scale, seq_lens=dev.seq_lens, block_table=dev.block_table,
+             max_blocks_per_seq=dev.max_blocks_per_seq, max_seq_len=dev.max_seq_len,
+             causal=dev.causal, softmax_scale=dev.softmax_scale, rope_base=dev.rope_base)
+    torch.cuda.synchronize()
+    return {"q_abs": _np(step.q_abs), "o_lat": _np(step.o_lat), "lse": _np(step.lse),
+            "o": _np(step.o), "num_splits": step.num_splits}
+
+
+def check_all_stages(inp, out, tol=None):
+    c = inp.cfg
+    tol = tol or tol_for(c)
+    ab = mla_absorbed(inp)
+    ref = mla_decode(inp)
+    errs = {
+        "q_lat": row_rel_err(out["q_abs"][..., :c.d_latent], ab["q_lat"]),
+        "q_pe": row_rel_err(out["q_abs"][..., c.d_latent:], ab["q_pe"]),
+        "o_lat": row_rel_err(out["o_lat"], ab["o_lat"]),
+        "o": row_rel_err(out["o"], ref["o"]),
+    }
+    fin = np.isfinite(ref["lse"])
+    assert np.array_equal(fin, np.isfinite(out["lse"])), "lse -inf pattern differs"
+    errs["lse"] = float(np.max(np.abs(out["lse"][fin] - ref["lse"][fin]))) if fin.any() else 0.0
+    print(c.name, {k: f"{v:.2e}" for k, v in errs.items()}, "splits", out["num_splits"], flush=True)
+    for k, v in errs.items():
+        assert v <= tol, (k, v, tol)
+    return errs
+
+
+# ---------------------------------------------------------------- fp32
+
+@pytest.mark.parametrize("splits", [None, 1, 2, 5])
+def test_tiny_f32(splits):
+    inp = MLAInputs(CONFIGS["tiny_f32"])
+    check_all_stages(inp, run_gpu(inp, num_splits=splits))
+
+
+F32_SMALL = scaled(CONFIGS["tiny_f32"], name="f32_ragged", batch=4, seq_len=0, len_lo=1, len_hi=300,
+                   heads=6, d_nope=24, d_rope=16, d_latent=40, d_v=20)
+
+
+@pytest.mark.parametrize("paged", [False, True])
+@pytest.mark.parametrize("q_len,causal", [(1, False), (2, True), (3, False)])
+@pytest.mark.parametrize("splits", [1, 3, 64])
+def test_f32_ragged(paged, q_len, causal, splits):
+    cfg = scaled(F32_SMALL, paged=paged, q_len=q_len, causal=causal, query_in_cache=causal)
+    inp = MLAInputs(cfg)
+    check_all_stages(inp, run_gpu(inp, num_splits=splits))
+
+
+def test_f32_split_invariance_and_paged_equals_contiguous():
+    base = scaled(F32_SMALL, batch=3)
+    outs = []
+    for paged in (False, True):
+        inp = MLAInputs(scaled(base, paged=paged))
+        for g in (1, 2, 7, 40):
+            outs.append(run_gpu(inp, num_splits=g))
+    for o in outs[1:]:
+        assert row_rel_err(o["o"], outs[0]["o"]) < 2e-6
+        assert np.max(np.abs(o["lse"] - outs[0]["lse"])) < 2e-6
+
+
+def test_f32_empty_sequence_and_single_token():
+    cfg = scaled(F32_SMALL, batch=3, len_lo=1, len_hi=65)
+    inp = MLAInputs(cfg)
+    inp.seq_lens[:] = [0, 1, 65]
+    inp.positions[:, 0] = inp.seq_lens
+    out = run_gpu(inp, num_splits=4)
+    assert np.all(out["o"][0] == 0) and np.all(out["lse"][0] == -np.inf)
+    ref = mla_decode(inp, rows=[(b, 0, h) for b in (1, 2) for h in range(cfg.heads)])
+    assert row_rel_err(out["o"][1:], ref["o"][1:]) < 1e-5
+
+
+# ---------------------------------------------------------------- bf16 / fp8
+
+DSV3_SMALL = scaled(CONFIGS["dsv3_b16_l4k"], name="dsv3_small", batch=2, seq_len=0,
+                    len_lo=65, len_hi=333)
+
+
+@pytest.mark.parametrize("flags", [mla.FLAG_GENERIC, 0])
+@pytest.mark.parametrize("paged", [False, True])
+def test_bf16_dsv3_small(flags, paged):
+    inp = MLAInputs(scaled(DSV3_SMALL, paged=paged))
+    check_all_stages(inp, run_gpu(inp, flags=flags, num_splits=5))
+
+
+FP8_SMALL = scaled(CONFIGS["fp8_b128_l16k_q2"], name="fp8_small", batch=2, seq_len=0,
+                   len_lo=70, len_hi=200)
+
+
+@pytest.mark.parametrize("flags", [mla.FLAG_GENERIC, 0])
+@pytest.mark.parametrize("paged", [False, True])
+def test_fp8_small_causal(flags, paged):
+    inp = MLAInputs(scaled(FP8_SMALL, paged=paged))
+    check_all_stages(inp, run_gpu(inp, flags=flags, num_splits=3))
