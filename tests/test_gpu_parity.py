@@ -128,3 +128,40 @@ FP8_SMALL = scaled(CONFIGS["fp8_b128_l16k_q2"], name="fp8_small", batch=2, seq_l
 def test_fp8_small_causal(flags, paged):
     inp = MLAInputs(scaled(FP8_SMALL, paged=paged))
     check_all_stages(inp, run_gpu(inp, flags=flags, num_splits=3))
+
+
+# ------------------------------------------------------- MFMA decode path
+
+BF16_RAGGED = scaled(CONFIGS["dsv3_b16_l4k"], name="bf16_ragged", batch=3, seq_len=0,
+                     len_lo=1, len_hi=700)
+
+
+@pytest.mark.parametrize("paged", [False, True])
+@pytest.mark.parametrize("q_len,causal", [(1, False), (2, True)])
+@pytest.mark.parametrize("splits", [1, 7, 300])
+def test_bf16_mfma_ragged(paged, q_len, causal, splits):
+    cfg = scaled(BF16_RAGGED, paged=paged, q_len=q_len, causal=causal, query_in_cache=causal)
+    inp = MLAInputs(cfg)
+    check_all_stages(inp, run_gpu(inp, num_splits=splits))
+
+
+def test_bf16_mfma_matches_generic_kernels():
+    inp = MLAInputs(scaled(BF16_RAGGED, paged=True, seed=99))
+    dev = to_device(inp)
+    a = run_gpu(inp, num_splits=5, dev=dev)
+    b = run_gpu(inp, flags=mla.FLAG_GENERIC, num_splits=5, dev=dev)
+    assert row_rel_err(a["o_lat"], b["o_lat"]) < 1e-2
+    assert np.max(np.abs(a["lse"] - b["lse"])) < 1e-2
+
+
+def test_bf16_mfma_32_heads_and_empty_sequence():
+    cfg = scaled(BF16_RAGGED, heads=32, batch=4, len_lo=1, len_hi=200)
+    inp = MLAInputs(cfg)
+    inp.seq_lens[:] = [130, 0, 64, 1]
+    inp.positions[:, 0] = inp.seq_lens
+    out = run_gpu(inp, num_splits=3)
+    assert np.all(out["o"][1] == 0) and np.all(out["lse"][1] == -np.inf)
+    rows = [(b, 0, h) for b in (0, 2, 3) for h in range(32)]
+    ref = mla_decode(inp, rows=rows)
+    for b in (0, 2, 3):
+        assert row_rel_err(out["o"][b], ref["o"][b]) < 2e-2
