@@ -1,0 +1,241 @@
+#!/usr/bin/env python3
+"""Benchmark one MLA absorbed-decode step on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+A step is the whole hot path on one batch of synthetic inputs already
+resident in GPU memory: mla_absorb_q (W_UK absorption + query RoPE),
+mla_decode_attn (split-K attention over the shared latent cache),
+mla_combine (log-sum-exp merge) and mla_out_proj (W_UV), all on one stream.
+The default workload is DeepSeek-V3 shaped: batch 64, 8192 cached tokens per
+sequence, 128 heads, latent 512 + RoPE 64, bf16, paged in 64-token blocks.
+
+Prints one JSON line on stdout.  `value` is cache GB/s of the whole step
+(cached bytes / step time); `ms_per_step` gives the step latency.  The
+`roofline` object rates the decode kernel alone, timed with HIP events on
+the stream it runs on.  `cpu_baseline` times the float64 CPU oracle on a
+bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0      # dense bf16 MFMA
+METRIC = "MLA decode µs/step, TFLOP/s and cache GB/s at B=64,L=8k,128 heads (% roofline)"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def accounting(inp):
+    """Algorithmic bytes and flops of one step (and of the decode kernel)."""
+    c = inp.cfg
+    tokens = int(inp.seq_lens.astype(np.int64).sum())
+    B, Lq, H = c.batch, c.q_len, c.heads
+    el = 4 if c.q_dtype == "f32" else 2
+    cache = tokens * c.storage_bytes_per_token()
+    w = (H * c.d_nope * c.d_latent + H * c.d_v * c.d_latent) * el
+    q = B * Lq * H * (c.d_nope + c.d_rope) * el
+    o = B * Lq * H * c.d_v * el
+    attn_flops = 2.0 * H * Lq * tokens * (c.d_latent + c.d_rope + c.d_latent)
+    proj_flops = 2.0 * B * Lq * H * (c.d_nope * c.d_latent + c.d_latent * c.d_v)
+    return dict(tokens=tokens, cache_bytes=cache, step_bytes=cache + w + q + o,
+                attn_flops=attn_flops, step_flops=attn_flops + proj_flops)
+
+
+def cpu_baseline(inp, seconds: float):
+    """Time the float64 oracle on a sample of (b, i, h) rows of the workload."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import mla_decode
+
+    c = inp.cfg
+    rows_all = [(b, i, h) for b in range(c.batch) for i in range(c.q_len) for h in range(c.heads)]
+    t0 = time.perf_counter()
+    mla_decode(inp, rows=rows_all[:1])
+    one = max(time.perf_counter() - t0, 1e-3)
+    n = int(max(1, min(len(rows_all), seconds / one)))
+    sample = rows_all[:n]
+    t0 = time.perf_counter()
+    mla_decode(inp, rows=sample)
+    dt = time.perf_counter() - t0
+    acc = accounting(inp)
+    # each query row covers 1/(B*Lq*H) of the step's work over the cache
+    frac = n / len(rows_all)
+    threads = max([t.get("num_threads", 1) for t in threadpool_info()] or [1])
+    return {"value": round(frac * acc["cache_bytes"] / dt / 1e9, 4), "unit": "GB/s",
+            "cores": int(threads), "kind": "oracle",
+            "sample": f"{n} of {len(rows_all)} (b,i,h) query rows of sequence(s) "
+                      f"{sorted(set(r[0] for r in sample))}, {dt:.1f} s; value scales the "
+                      f"sample's share of the step's cache bytes by its time"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--num-splits", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures the one-GPU path only (asked for {max(args.gpus, world)} GPUs); "
+              "the decode step has no multi-GPU mode in this build.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    if args.copy_calibration:
+        n = 1 << 28                                   # 2^28 float32 = 1 GiB
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": 4 * n, "copy_calibration_bytes_written": 4 * n}))
+        return
+
+    import mla_latent_kv_lat_amd as mla
+    from mla_inputs import CONFIGS, HEADLINE, MLAInputs
+    from mla_inputs.device import to_device
+
+    name = args.workload or HEADLINE
+    cfg = CONFIGS[name]
+    t0 = time.perf_counter()
+    inp = MLAInputs(cfg)
+    dev = to_device(inp)
+    torch.cuda.synchronize()
+    log(f"[bench] inputs for {name} ready in {time.perf_counter() - t0:.1f} s")
+
+    DT = {"f32": mla.F32, "bf16": mla.BF16, "fp8": mla.FP8_E4M3}
+    d = mla.dims(cfg.batch, cfg.q_len, cfg.heads, cfg.d_nope, cfg.d_rope, cfg.d_latent, cfg.d_v,
+                 DT[cfg.q_dtype], DT[cfg.kv_dtype])
+    step = mla.DecodeStep(d, num_splits=args.num_splits or None)
+    G = step.num_splits
+    stream = torch.cuda.current_stream()
+
+    def absorb():
+        mla.mla_absorb_q(d, dev.q_nope, dev.q_rope, dev.positions, dev.rope_base, dev.w_uk,
+                         step.q_abs, stream)
+
+    def decode():
+        mla.mla_decode_attn(d, step.q_abs, dev.latent, dev.rope, dev.kv_row_stride, dev.kv_scale,
+                            dev.seq_lens, dev.block_table, dev.max_blocks_per_seq,
+                            mla.TILE_TOKENS, dev.max_seq_len, dev.causal, dev.softmax_scale, G,
+                            step.o_part, step.lse_part, stream)
+
+    def combine():
+        mla.mla_combine(d, G, dev.seq_lens, step.o_part, step.lse_part, step.o_lat, step.lse,
+                        stream)
+
+    def out_proj():
+        mla.mla_out_proj(d, step.o_lat, dev.w_uv, step.o, stream)
+
+    parts = [absorb, decode, combine, out_proj]
+
+    for _ in range(args.warmup):
+        for f in parts:
+            f()
+    torch.cuda.synchronize()
+    if not torch.isfinite(step.o.float()).all():
+        raise RuntimeError("non-finite decode output")
+
+    # ---- timed region: exactly K steps
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        for f in parts:
+            f()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+
+    # ---- per-kernel durations (events around each launch, same stream)
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in parts] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for k in range(args.steps):
+        for f, (a, b) in zip(parts, evs[k]):
+            a.record(stream)
+            f()
+            b.record(stream)
+    torch.cuda.synchronize()
+    kern_ms = [float(np.mean([evs[k][j][0].elapsed_time(evs[k][j][1]) for k in range(args.steps)]))
+               for j in range(len(parts))]
+
+    acc = accounting(inp)
+    us_step = ms_step * 1e3
+    cache_gbs = acc["cache_bytes"] / (ms_step * 1e-3) / 1e9
+    tflops = acc["step_flops"] / (ms_step * 1e-3) / 1e12
+    t_roof = max(acc["step_flops"] / (PEAK_BF16_TFLOPS * 1e12), acc["step_bytes"] / (PEAK_HBM_GBS * 1e9))
+    dec_s = kern_ms[1] * 1e-3
+    dec_gbs = acc["cache_bytes"] / dec_s / 1e9
+    dec_tflops = acc["attn_flops"] / dec_s / 1e12
+
+    traffic = None
+    tpath = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                         "decode_mfma_b64_l8k_paged_counters.json")
+    if os.path.exists(tpath):
+        try:
+            with open(tpath) as f:
+                tr = json.load(f)
+            from mla_latent_kv_lat_amd.build import source_digest
+            if tr.get("source_digest") == source_digest() and tr.get("workload") == name:
+                traffic = tr.get("hbm_bytes_per_launch")
+        except Exception as e:  # a stale or unreadable summary just leaves traffic unknown
+            log(f"[bench] traffic summary not used: {e}")
+
+    out = {
+        "metric": METRIC,
+        "value": round(cache_gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "us_per_step": round(us_step, 2),
+        "tflops": round(tflops, 2),
+        "pct_roofline": round(100.0 * t_roof / (ms_step * 1e-3), 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.kv_dtype == "bf16" else ("fp8-cache/bf16" if cfg.kv_dtype == "fp8" else "f32"),
+        "data": "synthetic",
+        "config": {"workload": name, "batch": cfg.batch, "seq_len": cfg.max_seq_len,
+                   "cached_tokens": acc["tokens"], "heads": cfg.heads, "q_len": cfg.q_len,
+                   "d_latent": cfg.d_latent, "d_rope": cfg.d_rope, "d_nope": cfg.d_nope,
+                   "d_v": cfg.d_v, "paged_block": 64 if cfg.paged else 0,
+                   "kv_dtype": cfg.kv_dtype, "num_splits": G, "parallelism": "single GPU"},
+        "kernels_us": {"absorb_q": round(kern_ms[0] * 1e3, 2), "decode_attn": round(kern_ms[1] * 1e3, 2),
+                       "combine": round(kern_ms[2] * 1e3, 2), "out_proj": round(kern_ms[3] * 1e3, 2)},
+        "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(dec_gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
+                     "kernel": "decode_mfma_kernel",
+                     "mfma_tflops": round(dec_tflops, 1),
+                     "mfma_frac": round(dec_tflops / PEAK_BF16_TFLOPS, 4)},
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a sample ...")
+        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -23,6 +23,10 @@ template <> struct Store4<uint16_t> {
   }
 };
 
+// One wave per (sequence, query row).  The lanes first turn the partials'
+// LSEs into normalised weights (one unit per lane, 64 at a time), then stream
+// the 512-wide partial rows with 16-byte loads, keeping up to 8 units' loads
+// in flight per lane.
 template <typename OT>
 __global__ __launch_bounds__(256) void combine_kernel(int B, int R, int d_c, int G,
                                                       const int32_t* __restrict__ seq_lens,
@@ -39,39 +43,120 @@ __global__ __launch_bounds__(256) void combine_kernel(int B, int R, int d_c, int
   const int64_t tb = tiles_of(seq_lens[b]);
   OT* out = o_lat + ((int64_t)b * R + row) * d_c;
 
-  float mx = -INFINITY;
+  // units touching b: u0..u1 (empty units hold no partial: weight 0)
   int64_t u0 = 0, u1 = -1;
   if (tb > 0) {
     u0 = unit_of_tile(pb, T, G);
     u1 = unit_of_tile(pb + tb - 1, T, G);
-    for (int64_t u = u0 + lane; u <= u1; u += 64)
-      if (unit_begin(u, T, G) < unit_begin(u + 1, T, G))
-        mx = fmaxf(mx, lse_part[(u + b) * R + row]);
-    mx = wave_max(mx);
   }
-  if (mx == -INFINITY) {  // no token seen: zero output
+  const int n = (int)(u1 - u0 + 1);
+  auto live = [&](int64_t u) { return unit_begin(u, T, G) < unit_begin(u + 1, T, G); };
+
+  // Fast path (at most 8 units, d_c <= 512): every load of the row -- the
+  // partials and their LSEs -- is issued before any of them is needed.
+  constexpr int kU = 8, kC = 2;
+  if (n <= kU && d_c <= 256 * kC) {
+    float4 v[kU][kC];
+    float lu = -INFINITY;  // lane k < n holds unit u0 + k's LSE
+    if (lane < n && live(u0 + lane)) lu = lse_part[(u0 + lane + b) * R + row];
+#pragma unroll
+    for (int k = 0; k < kU; ++k) {
+      const int64_t u = u0 + k;
+      const bool ok = k < n && live(u);
+#pragma unroll
+      for (int j = 0; j < kC; ++j) {
+        const int c = lane * 4 + 256 * j;
+        v[k][j] = (ok && c < d_c) ? *(const float4*)(o_part + ((u + b) * R + row) * d_c + c)
+                                  : make_float4(0, 0, 0, 0);
+      }
+    }
+    const float mx = wave_max(lu);
+    if (mx == -INFINITY) {  // no token seen: zero output
+      for (int c = lane * 4; c < d_c; c += 256) Store4<OT>::run(out + c, make_float4(0, 0, 0, 0));
+      if (lse_out && lane == 0) lse_out[(int64_t)b * R + row] = -INFINITY;
+      return;
+    }
+    const float el = lu == -INFINITY ? 0.f : expf(lu - mx);
+    const float z = wave_sum(el);
+    const float wl = el / z;
+    float4 acc[kC];
+#pragma unroll
+    for (int j = 0; j < kC; ++j) acc[j] = make_float4(0, 0, 0, 0);
+#pragma unroll
+    for (int k = 0; k < kU; ++k) {
+      const float w = __shfl(wl, k, 64);
+#pragma unroll
+      for (int j = 0; j < kC; ++j) {
+        acc[j].x = fmaf(w, v[k][j].x, acc[j].x);
+        acc[j].y = fmaf(w, v[k][j].y, acc[j].y);
+        acc[j].z = fmaf(w, v[k][j].z, acc[j].z);
+        acc[j].w = fmaf(w, v[k][j].w, acc[j].w);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kC; ++j) {
+      const int c = lane * 4 + 256 * j;
+      if (c < d_c) Store4<OT>::run(out + c, acc[j]);
+    }
+    if (lse_out && lane == 0) lse_out[(int64_t)b * R + row] = mx + logf(z);
+    return;
+  }
+
+  // General path: many units or wide rows.
+  float mx = -INFINITY;
+  for (int k = lane; k < n; k += 64)
+    if (live(u0 + k)) mx = fmaxf(mx, lse_part[(u0 + k + b) * R + row]);
+  mx = wave_max(mx);
+  if (mx == -INFINITY) {
     for (int c = lane * 4; c < d_c; c += 256) Store4<OT>::run(out + c, make_float4(0, 0, 0, 0));
     if (lse_out && lane == 0) lse_out[(int64_t)b * R + row] = -INFINITY;
     return;
   }
   float z = 0.f;
-  for (int64_t u = u0 + lane; u <= u1; u += 64)
-    if (unit_begin(u, T, G) < unit_begin(u + 1, T, G))
-      z += expf(lse_part[(u + b) * R + row] - mx);
+  for (int k = lane; k < n; k += 64)
+    if (live(u0 + k)) z += expf(lse_part[(u0 + k + b) * R + row] - mx);
   z = wave_sum(z);
   const float inv_z = 1.f / z;
-  for (int c = lane * 4; c < d_c; c += 256) {
-    float4 acc = make_float4(0, 0, 0, 0);
-    for (int64_t u = u0; u <= u1; ++u) {
-      if (!(unit_begin(u, T, G) < unit_begin(u + 1, T, G))) continue;
-      const float w = expf(lse_part[(u + b) * R + row] - mx) * inv_z;
-      const float4 v = *(const float4*)(o_part + ((u + b) * R + row) * d_c + c);
-      acc.x = fmaf(w, v.x, acc.x);
-      acc.y = fmaf(w, v.y, acc.y);
-      acc.z = fmaf(w, v.z, acc.z);
-      acc.w = fmaf(w, v.w, acc.w);
+  for (int c0 = 0; c0 < d_c; c0 += 256 * kC) {
+    float4 acc[kC];
+#pragma unroll
+    for (int j = 0; j < kC; ++j) acc[j] = make_float4(0, 0, 0, 0);
+    for (int k0 = 0; k0 < n; k0 += 64) {
+      float wl = 0.f;
+      if (k0 + lane < n && live(u0 + k0 + lane))
+        wl = expf(lse_part[(u0 + k0 + lane + b) * R + row] - mx) * inv_z;
+      const int m = n - k0 < 64 ? n - k0 : 64;
+      for (int k1 = 0; k1 < m; k1 += kU) {
+        float4 v[kU][kC];
+#pragma unroll
+        for (int k2 = 0; k2 < kU; ++k2) {
+          const int64_t u = u0 + k0 + k1 + k2;
+          const bool ok = k1 + k2 < m && live(u);
+#pragma unroll
+          for (int j = 0; j < kC; ++j) {
+            const int c = c0 + lane * 4 + 256 * j;
+            v[k2][j] = (ok && c < d_c) ? *(const float4*)(o_part + ((u + b) * R + row) * d_c + c)
+                                       : make_float4(0, 0, 0, 0);
+          }
+        }
+#pragma unroll
+        for (int k2 = 0; k2 < kU; ++k2) {
+          const float w = __shfl(wl, k1 + k2, 64);
+#pragma unroll
+          for (int j = 0; j < kC; ++j) {
+            acc[j].x = fmaf(w, v[k2][j].x, acc[j].x);
+            acc[j].y = fmaf(w, v[k2][j].y, acc[j].y);
+            acc[j].z = fmaf(w, v[k2][j].z, acc[j].z);
+            acc[j].w = fmaf(w, v[k2][j].w, acc[j].w);
+          }
+        }
+      }
     }
-    Store4<OT>::run(out + c, acc);
+#pragma unroll
+    for (int j = 0; j < kC; ++j) {
+      const int c = c0 + lane * 4 + 256 * j;
+      if (c < d_c) Store4<OT>::run(out + c, acc[j]);
+    }
   }
   if (lse_out && lane == 0) lse_out[(int64_t)b * R + row] = mx + logf(z);
 }
