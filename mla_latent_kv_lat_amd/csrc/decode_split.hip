@@ -1,0 +1,526 @@
+// Split-K MLA decode for gfx950, bf16 cache, latent 512 + RoPE 64: the
+// scores and the value sum split the workgroup's waves differently.
+//
+// Pages cited (title, section):
+//   [ARCH] "Model Architecture Driving Inference Systems: From MHA/GQA to
+//          DeepSeek MLA Matrix Absorption and Memory Minimalism"
+//
+// One workgroup = one split-K unit x 128 query rows ((query i, head h) pairs,
+// row i*H + h), 8 waves.  Per 32-token sub-tile of the cache, staged once in
+// LDS for all 128 heads ([ARCH] 3.1: every head scores the same raw latent):
+//
+//   scores   wave w owns rows 16w..16w+15: S^T = K Q^T with
+//            v_mfma_f32_16x16x32_bf16 (K = tile rows from LDS as A, the
+//            wave's absorbed queries as B: 13 of the 18 k-slices in
+//            registers, the last 5 in LDS); online softmax in log2 units
+//            with a lazy rescale; P (bf16) goes to a small LDS buffer.
+//   values   wave w owns latent columns 64w..64w+63 for all 128 rows:
+//            O[:, cols] += P V[:, cols] with v_mfma_f32_32x32x16_bf16
+//            (P from LDS as A, V = the tile's latent part read transposed
+//            with ds_read_b64_tr_b16 as B).
+//
+// Reading only its own 64 columns of V (instead of all 512) is what this
+// split buys: the LDS read instructions per tile drop by ~40% against each
+// wave doing both products for its own heads.
+//
+// Operand layouts:
+//   16x16x32  A: lane l row l%16, k 8(l/16)..+7; B: column l%16, same k;
+//             C: column l%16, rows 4(l/16)..+3
+//   32x32x16  A: lane l row l%32, k 8(l/32)..+7; B: column l%32, same k;
+//             C: column l%32, rows 8(r/4) + 4(l/32) + r%4, r = 0..15
+// The order of k inside one MFMA is immaterial when A and B agree; P is
+// stored so that each lane's 16-byte A operand holds tokens
+// {16ks + 4hf + 0..3, 16ks + 8 + 4hf + 0..3}, the rows its two transposed V
+// reads return.
+//
+// Sub-tile LDS layout (32 rows x 72 16-byte chunks = 36 KB): 1 KB blocks of
+// 8 rows x 8 chunks, block (cg, rg) at (cg*4 + rg) KB; inside, row rho /
+// chunk kappa at entry 8*(kappa ^ (rg&1)) + (rho ^ 4*((kappa ^ kappa>>1)&1)),
+// which keeps the score reads and the transposed value reads free of bank
+// conflicts.  Each block is one wave-wide direct global->LDS load.  A ring of
+// 3 sub-tiles keeps two loads in flight ahead of the one being used.
+//
+// The loop is latency-bound before it is bandwidth-bound, so it avoids
+// anything that stalls a wave on memory: the unit's tile descriptors
+// (sequence, tokens left, first cache row) sit in the lanes of a VGPR window
+// and are read with v_readlane; the waits on the direct loads are counted by
+// hand; no register is spilled (a scratch reload would force a wait on every
+// load in flight).
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "common.hpp"
+#include "kernels.hpp"
+#include "mfma_common.hpp"
+
+namespace mla {
+namespace {
+
+using namespace mfma;
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+constexpr int kSub = 32;                       // tokens per LDS sub-tile
+constexpr int kSubBytes = kSub * 576 * 2;      // 36864
+constexpr int kRing = 3;
+constexpr int kPPitch = 80;                    // bytes per row of P (32 bf16 + pad)
+constexpr int kPBytes = 128 * kPPitch;         // 10240
+constexpr int kQReg = 13;                      // k-slices of Q kept in registers
+constexpr int kQLds = 18 - kQReg;              // the rest live in LDS
+constexpr int kOffP = kRing * kSubBytes;       // 110592
+constexpr int kOffAlpha = kOffP + kPBytes;     // 120832
+constexpr int kOffL = kOffAlpha + 512;         // 121344
+constexpr int kOffFlag = kOffL + 512;          // 121856
+constexpr int kOffQ = kOffFlag + 128;          // 121984
+constexpr int kLdsBytes = kOffQ + kQLds * 8192;  // 162944
+
+// Lane-resident descriptors of tiles wx .. wx+wn-1 of a unit's walk over
+// the cache: lane i describes tile wx+i (its sequence, the tokens from the
+// tile's start to the sequence end, and the tile's first cache row).  The hot
+// loop reads them with v_readlane, so no scalar-memory round trip sits on the
+// path from one sub-tile to the next.  Cache rows fit in 32 bits: 2^31 rows
+// of >= 1 KB would exceed any HBM.
+struct TileWin {
+  int64_t wx;      // first tile (uniform)
+  int wn;          // tiles described (uniform, 1..64)
+  int b0;          // sequence of tile wx ...
+  int64_t pb0;     // ... and the global index of its first tile (uniform)
+  int b, rem, row0;  // per lane
+};
+
+struct TileInfo {
+  int b;
+  int rem;       // tokens from the tile's first row to the sequence end (>= 1)
+  int64_t row0;  // first cache row of the tile
+};
+
+__device__ __forceinline__ int64_t readlane64(int64_t v, int i) {
+  const int lo = __builtin_amdgcn_readlane((int)(uint32_t)v, i);
+  const int hi = __builtin_amdgcn_readlane((int)(v >> 32), i);
+  return (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+
+// Describe tiles wx .. min(wx+64, x1)-1.  (b_s, pb_s): any sequence at or
+// before the one holding tile wx, and the global index of its first tile.
+// Sequence b ends at global tile E_b = sum of tiles of sequences <= b; tile x
+// lies in the first sequence with E_b > x, which is b_s plus the number of
+// sequences from b_s on that end at or before x (empty ones included).
+// Ends with all vector memory drained.
+__device__ void build_window(const DecodeArgs& a, int64_t wx, int64_t x1, int b_s, int64_t pb_s,
+                             int lane, TileWin& win) {
+  const int64_t x = wx + lane;
+  int cnt = 0;
+  int64_t start = pb_s, carry = pb_s;
+  for (int cb = b_s; cb < a.batch; cb += 64) {
+    const int seq = cb + lane;
+    int64_t incl = seq < a.batch ? tiles_of(a.seq_lens[seq]) : 0;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int64_t o = __shfl_up(incl, d, 64);
+      if (lane >= d) incl += o;
+    }
+    const int64_t e = carry + incl;
+    for (int j = 0; j < 64; ++j) {
+      const int64_t ej = readlane64(e, j);
+      if (ej <= x) {
+        ++cnt;
+        start = ej;
+      }
+    }
+    carry = readlane64(e, 63);
+    if (carry > wx + 63) break;
+  }
+  const bool ok = x < x1;  // then b < batch: tile x belongs to a real sequence
+  const int b = b_s + cnt;
+  const int tis = (int)(x - start);
+  const int len = ok ? a.seq_lens[b] : 0;
+  const int page = ok && a.block_table ? a.block_table[(int64_t)b * a.mbps + tis] : 0;
+  win.wx = wx;
+  win.wn = (int)min((int64_t)64, x1 - wx);
+  win.b0 = __builtin_amdgcn_readfirstlane(b);
+  win.pb0 = uniform64(start);
+  win.b = b;
+  win.rem = len - tis * kTile;
+  win.row0 = a.block_table ? page * kTile : (int)((int64_t)b * a.max_seq_len + (int64_t)tis * kTile);
+  wait_vm0();
+}
+
+__device__ __forceinline__ TileInfo tile_info(const TileWin& win, int64_t x) {
+  const int i = (int)(x - win.wx);
+  TileInfo t;
+  t.b = __builtin_amdgcn_readlane(win.b, i);
+  t.rem = __builtin_amdgcn_readlane(win.rem, i);
+  t.row0 = (int64_t)(uint32_t)__builtin_amdgcn_readlane(win.row0, i);
+  return t;
+}
+
+// Next 32-token sub-tile: second half of the tile, or the next tile.
+__device__ __forceinline__ void step_sub(int64_t& x, int& hh) {
+  if (hh) {
+    hh = 0;
+    ++x;
+  } else {
+    hh = 1;
+  }
+}
+
+// This wave's direct loads of half hh of tile t into LDS at `dst`: blocks
+// k = w + 8j (< 36), i.e. row group w&3, chunk groups (w>>2) + 2j; waves 0-3
+// issue 5 loads (j < 5), waves 4-7 issue 4.  Rows past the sequence end
+// re-read its last row (poisoned page tails are never touched); an empty
+// second half re-reads the first half's last row.
+struct DmaPlan {
+  const char* lat;
+  const char* rop;
+  uint32_t voff;
+  uint32_t dst;
+};
+
+__device__ __forceinline__ DmaPlan plan_sub(const DecodeArgs& a, const TileInfo& t, int hh,
+                                            uint32_t dst, int w, int lane) {
+  const int in_page = min(kTile, t.rem);  // >= 1
+  const int kappa = (lane >> 3) ^ (w & 1);
+  const int rho = (lane & 7) ^ (4 * ((kappa ^ (kappa >> 1)) & 1));
+  int r = 32 * hh + (w & 3) * 8 + rho;
+  r = r < in_page ? r : in_page - 1;
+  const int64_t stride = a.row_stride * 2;
+  DmaPlan p;
+  p.lat = (const char*)a.latent + t.row0 * stride;
+  p.rop = (const char*)a.rope + t.row0 * stride;
+  p.voff = (uint32_t)(r * stride) + (uint32_t)(kappa * 16);
+  p.dst = dst;
+  return p;
+}
+
+__device__ __forceinline__ void issue_one(const DmaPlan& p, int w, int j) {
+  const int cg = (w >> 2) + 2 * j;
+  const uint32_t m0 = p.dst + (uint32_t)((w + 8 * j) * 1024);
+  if (cg < 8)
+    lds_dma16(p.lat, p.voff + cg * 128, m0);
+  else
+    lds_dma16(p.rop, p.voff, m0);
+}
+
+__device__ __forceinline__ void issue_all(const DmaPlan& p, int w) {
+#pragma unroll
+  for (int j = 0; j < 5; ++j)
+    if (j < 4 || w < 4) issue_one(p, w, j);
+}
+
+// Per-lane LDS byte offsets of the operand reads.  Each is computed where it
+// is used from an opaque copy of the lane id: a handful of VALU ops, where
+// keeping them live across the loop would cost registers the accumulators
+// need.
+__device__ __forceinline__ int fresh_lane() {
+  int l = (int)(threadIdx.x & 63);
+  asm volatile("" : "+v"(l));
+  return l;
+}
+
+// Score A operand inside a sub-tile.  Sub-tile blocks of 8 rows x 8 chunks:
+// row rho / chunk kappa of block (cg, rg) at entry
+// 8*(kappa ^ (rg&1)) + (rho ^ 4*((kappa ^ kappa>>1)&1)).
+__device__ __forceinline__ uint32_t off_qk(int lane) {
+  const int g = lane >> 4, li = lane & 15;
+  const int g1 = (li >> 3) & 1;
+  const int fq = (g ^ (g >> 1)) & 1;
+  return (uint32_t)(g1 * 1024 + 128 * (g ^ g1) + 16 * ((lane & 7) ^ (4 * fq)));
+}
+
+// Value B operand: the two transposed 8-byte reads rd = 0, 1.
+__device__ __forceinline__ uint32_t off_pv(int lane, int w, int rd) {
+  const int li = lane & 15, hf = lane >> 5;
+  const int ch = (lane >> 4) & 1, bq = (li & 3) >> 1;
+  const int rho_v = 4 * hf + (li >> 2);
+  return (uint32_t)(w * 4096 + rd * 1024 + 256 * ch + 128 * (bq ^ rd) +
+                    16 * (rho_v ^ (4 * (bq ^ ch))) + 8 * (li & 1));
+}
+
+// This lane's P write and P (A operand) read.
+__device__ __forceinline__ uint32_t off_pw(int lane, int w) {
+  const int g = lane >> 4, li = lane & 15;
+  return (uint32_t)((16 * w + li) * kPPitch + (g & 1) * 16 + (g >> 1) * 8);
+}
+__device__ __forceinline__ uint32_t off_pr(int lane) {
+  return (uint32_t)((lane & 31) * kPPitch + (lane >> 5) * 16);
+}
+
+// Q k-slices held in LDS: rows of 64 B (row 16w + lane%16, chunk lane/16),
+// 16-byte chunk c of row r stored at chunk c ^ ((r >> 1) & 3).
+__device__ __forceinline__ uint32_t off_ql(int lane, int w) {
+  const int g = lane >> 4, li = lane & 15;
+  return (uint32_t)(kOffQ + (16 * w + li) * 64 + 16 * (g ^ ((li >> 1) & 3)));
+}
+
+__global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeArgs a) {
+  __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes];
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4, li = lane & 15;    // 16x16 operand coordinates
+  const int hf = lane >> 5, n32 = lane & 31;  // 32x32 operand coordinates
+  const int R = a.q_len * a.heads;
+  const int rowg = blockIdx.y * 128;
+  const int qrow0 = rowg + 16 * w;            // rows this wave scores
+  const bool qk_active = qrow0 < R;
+  const int qi = qk_active ? qrow0 / a.heads : 0;
+  const int h0 = qk_active ? qrow0 % a.heads : 0;
+  const int u = blockIdx.x;
+  const int my_loads = w < 4 ? 5 : 4;
+
+  int64_t T, unused;
+  wave_tile_sums(a.seq_lens, a.batch, 0, T, unused);
+  T = uniform64(T);
+  const int64_t x0 = unit_begin(u, T, a.num_splits);
+  const int64_t x1 = unit_begin(u + 1, T, a.num_splits);
+  if (x0 >= x1) return;  // uniform across the workgroup
+
+  TileWin win;
+  {
+    int b;
+    int64_t pb;
+    find_sequence(a.seq_lens, a.batch, x0, b, pb);
+    build_window(a, x0, x1, __builtin_amdgcn_readfirstlane(b), uniform64(pb), lane, win);
+  }
+
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_char*)smem;
+  char* pbuf = smem + kOffP;
+  float* alpha_buf = (float*)(smem + kOffAlpha);
+  float* lbuf = (float*)(smem + kOffL);
+  uint8_t* flags = (uint8_t*)(smem + kOffFlag);
+  const float sl2 = a.softmax_scale * kLog2e;
+
+  // ---- prologue: sub-tiles 0 and 1 of the unit (a unit has >= 1 tile = 2 subs)
+  const int64_t nsub = 2 * (x1 - x0);
+  int64_t cx = x0, px = x0;  // tile of the sub-tile in use / next to issue
+  int chh = 0, phh = 0;      // and its half
+  issue_all(plan_sub(a, tile_info(win, px), phh, lds0, w, lane), w);
+  step_sub(px, phh);
+  issue_all(plan_sub(a, tile_info(win, px), phh, lds0 + kSubBytes, w, lane), w);
+  step_sub(px, phh);
+
+  bf16x8 q[kQReg];
+  f32x16 o[4][2];
+  float m_run = -INFINITY, l_run = 0.f;
+  bool new_seg = true;
+  int slot = 0;
+
+  for (int64_t y = 0; y < nsub; ++y) {
+    const int ln = fresh_lane();
+    const TileInfo ci = tile_info(win, cx);
+    if (new_seg) {
+      new_seg = false;
+      {  // unconditional (inactive waves read row 0) so q is dead between segments
+        const bf16x8* qp = (const bf16x8*)((const uint16_t*)a.q_abs +
+                                            (((int64_t)ci.b * a.q_len + qi) * a.heads + h0 + li) * 576);
+#pragma unroll
+        for (int kk = 0; kk < kQReg; ++kk) q[kk] = qp[4 * kk + g];
+#pragma unroll
+        for (int kk = kQReg; kk < 18; ++kk)
+          *(bf16x8*)(smem + off_ql(ln, w) + (kk - kQReg) * 8192) = qp[4 * kk + g];
+      }
+      wait_vm0();
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) o[mb][0] = o[mb][1] = f32x16{};
+      m_run = -INFINITY;
+      l_run = 0.f;
+    }
+    // sub-tile y has landed (the only newer loads are sub-tile y+1's)
+    if (y + 1 < nsub)
+      wait_vm(my_loads);
+    else
+      wait_vm(0);
+    block_sync();  // visible to all; everyone also finished sub-tile y-1
+    // the loads of sub-tile y+2, into the slot every wave finished with
+    if (y + 2 < nsub) {
+      const int s2 = slot + 2 >= kRing ? slot + 2 - kRing : slot + 2;
+      if (px >= win.wx + win.wn)  // slide the window to start at the tile in use
+        build_window(a, cx, x1, win.b0, win.pb0, ln, win);
+      issue_all(plan_sub(a, tile_info(win, px), phh, lds0 + (uint32_t)(s2 * kSubBytes), w, ln), w);
+      step_sub(px, phh);
+    }
+
+    const char* tile = smem + slot * kSubBytes;
+    char* pb = pbuf;  // one P buffer: the barrier at the top of the next
+                      // sub-tile orders its reuse after every wave's reads
+    const bool has_tokens = 32 * chh < ci.rem;  // uniform: an empty second half does nothing
+    // visible tokens of this sub-tile: all up to the sequence end, or with
+    // the causal mask those up to the query's own position
+    int nv = ci.rem - 32 * chh - (a.causal ? a.q_len - 1 - qi : 0);
+    nv = nv < 0 ? 0 : (nv > kSub ? kSub : nv);
+    const bool scores = has_tokens && qk_active && nv > 0;  // uniform per wave
+    if (has_tokens) {
+      // ---------------- scores and softmax for this wave's 16 rows
+      bf16x8 pw = bf16x8{};
+      bool need = false;
+      float alpha = 1.f;
+      if (scores) {
+        f32x4 s[2] = {f32x4{}, f32x4{}};
+        constexpr int kPf = 2;
+        const int lq = fresh_lane();
+        const uint32_t o_qk = off_qk(lq), o_ql = off_ql(lq, w);
+        bf16x8 ka[kPf + 1][2], qb[kPf + 1];
+        auto kload = [&](int kk) {
+          const int e = kk % (kPf + 1);
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            ka[e][j] = *(const bf16x8*)(tile + (uint32_t)((kk >> 1) * 4096 + 2048 * j + 512 * (kk & 1)) + o_qk);
+          if (kk >= kQReg) qb[e] = *(const bf16x8*)(smem + o_ql + (kk - kQReg) * 8192);
+        };
+#pragma unroll
+        for (int kk = 0; kk < kPf; ++kk) kload(kk);
+#pragma unroll
+        for (int kk = 0; kk < 18; ++kk) {
+          if (kk + kPf < 18) kload(kk + kPf);
+          const int e = kk % (kPf + 1);
+          const bf16x8 qk = kk < kQReg ? q[kk < kQReg ? kk : 0] : qb[e];
+          s[0] = mfma16(ka[e][0], qk, s[0]);
+          s[1] = mfma16(ka[e][1], qk, s[1]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if (nv < kSub) {  // mask the tokens past the visible end
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (16 * j + 4 * (ln >> 4) + r >= nv) s[j][r] = -INFINITY;
+        }
+        // this lane's max over its 8 scores, in log2 units
+        const float lm = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                               fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3]))) * sl2;
+        // Rescale only when some score passes its row's running max by more
+        // than 2^8 (log2 units): the exponentials stay <= 256 and the final
+        // normalisation uses the same reference max for numerator and
+        // denominator.  Only then is the row max reduced across lanes.
+        need = __ballot(lm > m_run + 8.f) != 0;
+        if (need) {
+          float mt = fmaxf(lm, __shfl_xor(lm, 16, 64));
+          mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+          const float m_new = fmaxf(m_run, mt);
+          alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+          m_run = m_new;
+          l_run *= alpha;
+        }
+        // exponent arguments are <= 8; results under 2^-126 flush to zero
+        const float m_use = m_run == -INFINITY ? 0.f : m_run;
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float e = __builtin_amdgcn_exp2f(fmaf(s[j][r], sl2, -m_use));
+            l_run += e;
+            pw[4 * j + r] = (__bf16)e;
+          }
+      }
+      // P rows of this wave's heads (zeros when it has nothing to score)
+      {
+        const uint32_t o_pw = off_pw(fresh_lane(), w);
+        *(bf16x4*)(pb + o_pw) = __builtin_shufflevector(pw, pw, 0, 1, 2, 3);
+        *(bf16x4*)(pb + o_pw + 32) = __builtin_shufflevector(pw, pw, 4, 5, 6, 7);
+      }
+      // every wave publishes its factors (1 when unchanged): a rescale reads all rows
+      if ((ln >> 4) == 0) alpha_buf[16 * w + (ln & 15)] = alpha;
+      if (lane == 0) flags[w] = need ? 1 : 0;
+      block_sync();
+
+      // ---------------- rescale (rare), then O[:, 64w..] += P V
+      const uint64_t fl = *(const uint64_t*)flags;
+      if (fl != 0) {
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+          f32x16 a16;
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const f32x4 a4 = *(const f32x4*)(alpha_buf + mb * 32 + 8 * r4 + 4 * (ln >> 5));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a16[4 * r4 + i] = a4[i];
+          }
+          o[mb][0] *= a16;
+          o[mb][1] *= a16;
+          __builtin_amdgcn_sched_barrier(0);  // one block's factors live at a time
+        }
+      }
+      const int lv = fresh_lane();
+      const uint32_t o_pr = off_pr(lv), o_pv0 = off_pv(lv, w, 0), o_pv1 = off_pv(lv, w, 1);
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        bf16x8 pa[4], vb[2];
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+          pa[mb] = *(const bf16x8*)(pb + o_pr + (uint32_t)(mb * 32 * kPPitch + ks * 32));
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+          const uint32_t cb = (uint32_t)(2048 * ks + 512 * nb);
+          vb[nb] = cat(lds_tr4(tile, cb + o_pv0), lds_tr4(tile, cb + o_pv1));
+        }
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb) o[mb][nb] = mfma32(pa[mb], vb[nb], o[mb][nb]);
+      }
+    }
+
+    // ---- end of this unit's part of the sequence: write the partial
+    const bool last = y + 1 >= nsub || (chh == 1 && ci.rem <= kTile);
+    if (last) {
+      float l_tot = l_run + __shfl_xor(l_run, 16, 64);
+      l_tot += __shfl_xor(l_tot, 32, 64);
+      const int64_t sl = (int64_t)u + ci.b;
+      if ((ln >> 4) == 0) {
+        lbuf[16 * w + (ln & 15)] = l_tot;
+        if (qk_active)
+          a.lse_part[sl * R + qrow0 + (ln & 15)] =
+              l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+      }
+      block_sync();
+      // rows past R fall outside the resource and are dropped
+      const int rows_here = min(128, R - rowg);
+      const __amdgpu_buffer_rsrc_t rs =
+          buffer_rsrc(a.o_part + (sl * R + rowg) * 512, (uint32_t)rows_here * 2048u);
+      const uint32_t vo = (uint32_t)((4 * hf * 512 + 64 * w + n32) * 4);
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        f32x16 inv16;
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const f32x4 l4 = *(const f32x4*)(lbuf + mb * 32 + 8 * r4 + 4 * hf);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) inv16[4 * r4 + i] = l4[i] > 0.f ? 1.f / l4[i] : 0.f;
+        }
+        const f32x16 v0 = o[mb][0] * inv16, v1 = o[mb][1] * inv16;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const uint32_t so = (uint32_t)((mb * 32 + 8 * (r >> 2) + (r & 3)) * 2048);
+          buffer_store_f32(v0[r], rs, vo, so);
+          buffer_store_f32(v1[r], rs, vo + 128, so);
+        }
+      }
+      new_seg = true;
+    }
+    step_sub(cx, chh);
+    slot = slot + 1 >= kRing ? 0 : slot + 1;
+  }
+}
+
+}  // namespace
+
+bool mfma_decode_supports(const mla_dims_t& d, int64_t row_stride, const void* latent,
+                          const void* rope) {
+  return d.q_dtype == MLA_BF16 && d.kv_dtype == MLA_BF16 && d.d_latent == 512 &&
+         d.d_rope == 64 && d.heads % 16 == 0 && (row_stride * 2) % 16 == 0 &&
+         ((uintptr_t)latent & 15) == 0 && ((uintptr_t)rope & 15) == 0;
+}
+
+hipError_t launch_decode_mfma(const mla_dims_t& d, const DecodeArgs& a, hipStream_t s) {
+  const int R = d.q_len * d.heads;
+  dim3 grid((unsigned)a.num_splits, (unsigned)((R + 127) / 128));
+  hipLaunchKernelGGL(decode_split_kernel, grid, dim3(512), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace mla

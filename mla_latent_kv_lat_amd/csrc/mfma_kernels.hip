@@ -1,5 +1,6 @@
-// Matrix-core (MFMA) kernels for gfx950: bf16 queries and weights, bf16 or
-// fp8 cache, DeepSeek-V3 widths (latent 512, RoPE 64).
+// Matrix-core (MFMA) kernels for gfx950 around the attention: query
+// absorption of W_UK with RoPE, and the W_UV output projection (bf16).
+// The split-K decode itself lives in decode_split.hip.
 //
 // Pages cited (title, section):
 //   [ARCH] "Model Architecture Driving Inference Systems: From MHA/GQA to
@@ -10,8 +11,6 @@
 //   A (32 x 16): lane l holds row l%32, k = 8*(l/32) .. +7
 //   B (16 x 32): lane l holds column l%32, k = 8*(l/32) .. +7
 //   C (32 x 32): lane l holds column l%32, rows 8*(r/4) + 4*(l/32) + r%4
-// The order of k inside one instruction is immaterial as long as A and B
-// agree, which lets P stay in the registers the score MFMA wrote it to.
 //
 // ds_read_b64_tr_b16: in each group of 16 lanes, lane i names 4 consecutive
 // 16-bit elements (row i/4, columns 4*(i%4)..+3 of a 4 x 16 block) and gets
@@ -22,337 +21,12 @@
 
 #include "common.hpp"
 #include "kernels.hpp"
+#include "mfma_common.hpp"
 
 namespace mla {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef __attribute__((address_space(3))) char lds_char;
-typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
-
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
-
-__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ bf16x4 lds_tr4(const char* base, uint32_t off) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)((lds_char*)base + off));
-}
-
-__device__ __forceinline__ bf16x8 cat(bf16x4 a, bf16x4 b) {
-  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-
-// One 16-byte direct global->LDS load per lane: lane i reads 16 bytes at
-// sbase + voff (sbase wave-uniform, voff per lane) and the wave's 64 lanes fill
-// the 1 KB of LDS starting at byte address m0 in lane order.  Issued as
-// inline assembly so that waits on it are placed by hand (vmcnt), instead of
-// the compiler's blanket wait before every later LDS read.
-__device__ __forceinline__ void lds_dma16(const void* sbase, uint32_t voff, uint32_t m0) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(m0), "v"(voff),
-               "s"(sbase)
-               : "memory", "m0");
-}
-__device__ __forceinline__ int64_t uniform64(int64_t v) {
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)(uint64_t)v);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
-  return (int64_t)(((uint64_t)hi << 32) | lo);
-}
-// vmcnt(0) through the builtin, so the compiler's own wait bookkeeping also
-// sees every earlier vector load as complete (and places no later waits for
-// them, which would otherwise land on the next tile's prefetch).
-__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0f70); }
-__device__ __forceinline__ void block_sync() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-// ===================================================================== decode
-//
-// One workgroup = one split-K unit x one group of 128 query rows (rows are
-// (query i, head h) pairs, i*H + h).  8 waves, each owning 16 rows: the heads
-// sit on an MFMA dimension, so one pass over a cached tile in LDS serves all
-// 128 heads ([ARCH] 3.1: every head scores the same raw cached latent).
-//
-// Per 64-token tile (bf16: 64 rows x 576 = 72 KB, double-buffered in LDS),
-// in two halves of 32 tokens:
-//   S^T[t, h] = sum_c K[t, c] Q[h, c]   K = tile (LDS), Q = q_abs (registers)
-//   online softmax over t (per head), in log2 units
-//   O[h, c]  += sum_t P[h, t] V[t, c]   V = tile latent part (LDS, transposed
-//                                        reads), O = fp32 accumulators
-// with v_mfma_f32_16x16x32_bf16, whose operand layouts are
-//   A (16 x 32): lane l holds row l%16, k = 8*(l/16) .. +7
-//   B (32 x 16): lane l holds column l%16, k = 8*(l/16) .. +7
-//   C (16 x 16): lane l holds column l%16, rows 4*(l/16) .. +3
-// The order of k inside one instruction is immaterial as long as A and B
-// agree, so P is used as the A operand right where the score MFMA left it.
-//
-// LDS tile layout: 1 KB blocks of 8 rows x 8 chunks (chunk = 16 bytes), block
-// (cg, rg) at ((cg*8 + rg) KB) for chunk group cg (0..8) and row group rg
-// (0..7).  Inside a block, row rho / chunk kappa sits at entry
-//   8*(kappa ^ (rg&1)) + (rho ^ 4*((kappa ^ kappa>>1) & 1))
-// which keeps both the score reads (16 rows x one chunk) and the transposed
-// value reads (8 rows x 2 chunks) free of bank conflicts.  One block is
-// exactly one wave-wide 16-byte direct load: 8 rows x 128 contiguous bytes.
-
-constexpr int kRowsPerWG = 128;
-constexpr int kWaves = 8;
-constexpr int kTileBytesBF16 = kTile * 576 * 2;  // 73728
-
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-struct TileRef {
-  int t0;       // first token of the tile
-  int n_tok;    // cached tokens of the sequence (rows past it are clamped)
-  int64_t row0; // cache row of token t0
-};
-
-__device__ __forceinline__ TileRef tile_ref(const DecodeArgs& a, int b, int64_t tile_in_seq) {
-  TileRef r;
-  r.t0 = (int)tile_in_seq * kTile;
-  r.n_tok = a.seq_lens[b];
-  r.row0 = a.block_table ? (int64_t)a.block_table[(int64_t)b * a.mbps + tile_in_seq] * kTile
-                         : (int64_t)b * a.max_seq_len + r.t0;
-  return r;
-}
-
-// Issue this wave's 9 of the tile's 72 block loads (bf16 cache): row group
-// rg = w, all 9 chunk groups.  Rows past the end of the sequence are clamped
-// to its last row, so poisoned tail slots of a page are never read.
-__device__ __forceinline__ void issue_tile_bf16(const DecodeArgs& a, const TileRef& tr,
-                                                uint32_t lds_base, int w, int lane) {
-  const int kappa = (lane >> 3) ^ (w & 1);
-  const int rho = (lane & 7) ^ (4 * ((kappa ^ (kappa >> 1)) & 1));
-  const int nvalid = tr.n_tok - tr.t0;  // >= 1
-  int r = w * 8 + rho;
-  r = r < nvalid ? r : nvalid - 1;
-  const int64_t stride = a.row_stride * 2;  // bytes
-  const char* lat = (const char*)a.latent + tr.row0 * stride;  // uniform
-  const char* rop = (const char*)a.rope + tr.row0 * stride;    // uniform
-  const uint32_t voff = (uint32_t)(r * stride) + (uint32_t)(kappa * 16);
-#pragma unroll
-  for (int cg = 0; cg < 8; ++cg)
-    lds_dma16(lat, voff + cg * 128, lds_base + (uint32_t)((cg * 8 + w) * 1024));
-  lds_dma16(rop, voff, lds_base + (uint32_t)((64 + w) * 1024));
-}
-
-template <int KV>  // KV: MLA_BF16
-__global__ __launch_bounds__(512, 1) void decode_mfma_kernel(DecodeArgs a) {
-  __shared__ __attribute__((aligned(1024))) char smem[2 * kTileBytesBF16];
-
-  const int lane = threadIdx.x & 63;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int g = lane >> 4;     // lane group (k slice of the MFMA operands)
-  const int li = lane & 15;    // this lane's head (column) within the wave
-  const int R = a.q_len * a.heads;
-  const int u = blockIdx.x;
-  const int row0 = blockIdx.y * kRowsPerWG + w * 16;  // first query row of this wave
-  const bool active = row0 < R;
-  const int qi = active ? row0 / a.heads : 0;          // query token of this wave
-  const int h0 = active ? row0 % a.heads : 0;
-
-  int64_t T, unused;
-  wave_tile_sums(a.seq_lens, a.batch, 0, T, unused);
-  T = uniform64(T);
-  const int64_t x0 = unit_begin(u, T, a.num_splits);
-  const int64_t x1 = unit_begin(u + 1, T, a.num_splits);
-  if (x0 >= x1) return;  // uniform across the workgroup
-
-  int cur_b;
-  int64_t cur_pb;
-  find_sequence(a.seq_lens, a.batch, x0, cur_b, cur_pb);
-  cur_b = __builtin_amdgcn_readfirstlane(cur_b);
-  cur_pb = uniform64(cur_pb);
-
-  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_char*)smem;
-  const float sl2 = a.softmax_scale * kLog2e;
-
-  // ---- per-lane constant parts of the LDS read addresses --------------------
-  // score reads: token row 16*j + li, chunk 4*kk + g
-  const int fq = (g ^ (g >> 1)) & 1;
-  const uint32_t qk_off = (uint32_t)(((li >> 3) & 1) * 1024 + 128 * (g ^ ((li >> 3) & 1)) +
-                                     16 * ((lane & 7) ^ (4 * fq)));
-  // value reads (transposed): token row 16*rd + 4*g + li/4, column 16*nb + 4*(li%4)
-  const int bq = (li & 3) >> 1;
-  const int rho_v = 4 * (g & 1) + (li >> 2);
-  uint32_t pv_off[2];
-#pragma unroll
-  for (int par = 0; par < 2; ++par)
-    pv_off[par] = (uint32_t)((g >> 1) * 1024 + 128 * (bq ^ (g >> 1)) +
-                             16 * (rho_v ^ (4 * (bq ^ par))) + 8 * (li & 1));
-
-  // ---- first tile of the unit ------------------------------------------------
-  int64_t x = x0;
-  issue_tile_bf16(a, tile_ref(a, cur_b, x - cur_pb), lds0, w, lane);
-
-  bf16x8 q[18];
-  f32x4 o[32];
-  float m_run = -INFINITY, l_run = 0.f;
-  bool new_seg = true;
-  int buf = 0;
-
-  while (x < x1) {
-    const int len = a.seq_lens[cur_b];
-    const int64_t tb = tiles_of(len);
-    const int64_t tis = x - cur_pb;  // tile index within the sequence
-    if (new_seg) {
-      // new segment: load this wave's 16 query rows, reset the state
-      new_seg = false;
-      const bf16x8* qp = (const bf16x8*)((const uint16_t*)a.q_abs +
-                                          (((int64_t)cur_b * a.q_len + qi) * a.heads + h0 + li) * 576);
-#pragma unroll
-      for (int kk = 0; kk < 18; ++kk) q[kk] = qp[4 * kk + g];
-#pragma unroll
-      for (int nb = 0; nb < 32; ++nb) o[nb] = f32x4{};
-      m_run = -INFINITY;
-      l_run = 0.f;
-    }
-    const int n_vis = a.causal ? len - a.q_len + qi + 1 : len;
-    int nv = n_vis - (int)tis * kTile;  // visible tokens of this tile for this wave
-    nv = nv < 0 ? 0 : (nv > kTile ? kTile : nv);
-
-    // next tile of the unit (possibly in a later sequence)
-    const int64_t xn = x + 1;
-    const bool seg_end = xn >= x1 || xn >= cur_pb + tb;
-    int nb_b = cur_b;
-    int64_t nb_pb = cur_pb;
-    if (xn < x1 && xn >= cur_pb + tb) {
-      nb_pb = cur_pb + tb;
-      ++nb_b;
-      while (tiles_of(a.seq_lens[nb_b]) == 0) ++nb_b;
-    }
-
-    wait_vm0();     // this wave's loads of tile x have landed
-    block_sync();   // ... and everyone's; everyone also finished tile x-1
-    if (xn < x1)
-      issue_tile_bf16(a, tile_ref(a, nb_b, xn - nb_pb),
-                      lds0 + (uint32_t)((buf ^ 1) * kTileBytesBF16), w, lane);
-
-    const char* tile = smem + buf * kTileBytesBF16;
-    if (active && nv > 0) {
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        if (32 * h2 >= nv) break;
-        // ---------------- scores for tokens 32*h2 .. +31: two 16 x 16 blocks,
-        // interleaved, with the tile reads issued kPf steps ahead
-        constexpr int kPf = 2;
-        f32x4 s[2] = {f32x4{}, f32x4{}};
-        bf16x8 ka[kPf + 1][2];
-        auto kload = [&](int kk, int j) {
-          const uint32_t off = (uint32_t)((kk >> 1) * 8192 + (2 * h2 + j) * 2048 +
-                                          512 * (kk & 1)) + qk_off;
-          return *(const bf16x8*)(tile + off);
-        };
-#pragma unroll
-        for (int kk = 0; kk < kPf; ++kk) {
-          ka[kk][0] = kload(kk, 0);
-          ka[kk][1] = kload(kk, 1);
-        }
-#pragma unroll
-        for (int kk = 0; kk < 18; ++kk) {
-          if (kk + kPf < 18) {
-            ka[(kk + kPf) % (kPf + 1)][0] = kload(kk + kPf, 0);
-            ka[(kk + kPf) % (kPf + 1)][1] = kload(kk + kPf, 1);
-          }
-          s[0] = mfma16(ka[kk % (kPf + 1)][0], q[kk], s[0]);
-          s[1] = mfma16(ka[kk % (kPf + 1)][1], q[kk], s[1]);
-          __builtin_amdgcn_sched_barrier(0);  // keep each prefetch in its step
-        }
-        // ---------------- online softmax (log2 domain)
-        float mt = -INFINITY;
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int t = 32 * h2 + 16 * j + 4 * g + r;
-            const float v = t < nv ? s[j][r] * sl2 : -INFINITY;
-            s[j][r] = v;
-            mt = fmaxf(mt, v);
-          }
-        mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-        mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-        const float m_new = fmaxf(m_run, mt);
-        // Rescale only when the running max grows by more than 2^8: the
-        // exponentials stay <= 256, and the final normalisation uses the
-        // same reference max for numerator and denominator, so the result
-        // is unchanged.
-        const bool rescale = __ballot(m_new > m_run + 8.f) != 0;
-        f32x4 a4 = f32x4{1.f, 1.f, 1.f, 1.f};
-        if (rescale) {
-          // 0 when m_run = -inf; 1 for a head that has seen no token yet
-          const float alpha = m_new == -INFINITY ? 1.f : exp2f(m_run - m_new);
-          m_run = m_new;
-          l_run *= alpha;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) a4[r] = __shfl(alpha, 4 * g + r, 64);
-        }
-        const float m_use = m_run == -INFINITY ? 0.f : m_run;
-        bf16x8 p;
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float e = exp2f(s[j][r] - m_use);
-            l_run += e;
-            p[4 * j + r] = (__bf16)e;
-          }
-        // ---------------- O = a4 * O + P V for tokens 32*h2 .. +31; the
-        // rescaling pass only runs when some head's running max moved.
-        if (rescale) {
-#pragma unroll
-          for (int nb = 0; nb < 32; ++nb) o[nb] *= a4;
-        }
-        const uint32_t kbase = (uint32_t)(h2 * 4096);
-        constexpr int kPv = 3;
-        bf16x8 vb[kPv + 1];
-        auto vload = [&](int nb) {
-          const uint32_t cb = (uint32_t)((nb >> 2) * 8192 + 256 * (nb & 3)) + kbase;
-          return cat(lds_tr4(tile, cb + pv_off[nb & 1]), lds_tr4(tile, cb + 2048 + pv_off[nb & 1]));
-        };
-#pragma unroll
-        for (int nb = 0; nb < kPv; ++nb) vb[nb] = vload(nb);
-#pragma unroll
-        for (int nb = 0; nb < 32; ++nb) {
-          if (nb + kPv < 32) vb[(nb + kPv) % (kPv + 1)] = vload(nb + kPv);
-          o[nb] = mfma16(p, vb[nb % (kPv + 1)], o[nb]);
-          __builtin_amdgcn_sched_barrier(0);  // keep each prefetch in its step
-        }
-      }
-    }
-
-    if (seg_end) {
-      if (active) {
-        const int64_t slot = (int64_t)u + cur_b;
-        float l_tot = l_run + __shfl_xor(l_run, 16, 64);
-        l_tot += __shfl_xor(l_tot, 32, 64);
-        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-        if (g == 0)
-          a.lse_part[slot * R + row0 + li] =
-              l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
-        float* op = a.o_part + (slot * R + row0) * 512;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int hr = 4 * g + r;
-          const float ir = __shfl(inv, hr, 64);
-#pragma unroll
-          for (int nb = 0; nb < 32; ++nb) op[(int64_t)hr * 512 + nb * 16 + li] = o[nb][r] * ir;
-        }
-      }
-      new_seg = true;
-    }
-    x = xn;
-    cur_b = nb_b;
-    cur_pb = nb_pb;
-    buf ^= 1;
-  }
-}
+using namespace mfma;
 
 // ===================================================================== absorb
 // q_abs[m, h, 0:d_c] = q_nope[m, h, :] W_UK[h]   ([ARCH] 3.1 absorbed query)
@@ -515,20 +189,6 @@ hipError_t launch_absorb_mfma(const mla_dims_t& d, const void* q_nope, const voi
                      (const uint16_t*)q_nope, (const uint16_t*)q_rope, positions,
                      (double)rope_base, (const uint16_t*)w_uk, (uint16_t*)q_abs, M, d.heads,
                      d.d_nope, d.d_rope, d.d_latent);
-  return hipGetLastError();
-}
-
-bool mfma_decode_supports(const mla_dims_t& d, int64_t row_stride, const void* latent,
-                          const void* rope) {
-  return d.q_dtype == MLA_BF16 && d.kv_dtype == MLA_BF16 && d.d_latent == 512 &&
-         d.d_rope == 64 && d.heads % 16 == 0 && (row_stride * 2) % 16 == 0 &&
-         ((uintptr_t)latent & 15) == 0 && ((uintptr_t)rope & 15) == 0;
-}
-
-hipError_t launch_decode_mfma(const mla_dims_t& d, const DecodeArgs& a, hipStream_t s) {
-  const int R = d.q_len * d.heads;
-  dim3 grid((unsigned)a.num_splits, (unsigned)((R + kRowsPerWG - 1) / kRowsPerWG));
-  hipLaunchKernelGGL(decode_mfma_kernel<MLA_BF16>, grid, dim3(kWaves * 64), 0, s, a);
   return hipGetLastError();
 }
 
