@@ -70,14 +70,25 @@ constexpr int kSubBytes = kSub * 576 * 2;      // 36864
 constexpr int kRing = 3;
 constexpr int kPPitch = 80;                    // bytes per row of P (32 bf16 + pad)
 constexpr int kPBytes = 128 * kPPitch;         // 10240
-constexpr int kQReg = 13;                      // k-slices of Q kept in registers
-constexpr int kQLds = 18 - kQReg;              // the rest live in LDS
-constexpr int kOffP = kRing * kSubBytes;       // 110592
-constexpr int kOffAlpha = kOffP + kPBytes;     // 120832
-constexpr int kOffL = kOffAlpha + 512;         // 121344
-constexpr int kOffFlag = kOffL + 512;          // 121856
-constexpr int kOffQ = kOffFlag + 128;          // 121984
-constexpr int kLdsBytes = kOffQ + kQLds * 8192;  // 162944
+constexpr int kF8Stage = 32 * 512 + 32 * 64 + 256;  // 18688: fp8 rows + scales
+
+// LDS map.  bf16 cache: the ring of three sub-tiles is the tile itself.
+// fp8 cache: the ring stages raw e4m3 rows and per-token scales, and one
+// bf16 tile receives the exact conversion of the sub-tile in use.
+template <bool F8>
+struct Lds {
+  // k-slices of Q (32 columns each) kept in registers; the rest live in LDS
+  static constexpr int kQReg = F8 ? 11 : 13;
+  static constexpr int kQLds = 18 - kQReg;
+  static constexpr int kStage = F8 ? kF8Stage : kSubBytes;  // bytes per ring slot
+  static constexpr int kConv = kRing * kStage;               // fp8: converted tile
+  static constexpr int kOffP = F8 ? kConv + kSubBytes : kRing * kSubBytes;
+  static constexpr int kOffAlpha = kOffP + kPBytes;
+  static constexpr int kOffL = kOffAlpha + 512;
+  static constexpr int kOffFlag = kOffL + 512;
+  static constexpr int kOffQ = kOffFlag + 128;
+  static constexpr int kBytes = kOffQ + kQLds * 8192;  // bf16 162944, fp8 161664
+};
 
 // Lane-resident descriptors of tiles wx .. wx+wn-1 of a unit's walk over
 // the cache: lane i describes tile wx+i (its sequence, the tokens from the
@@ -212,6 +223,85 @@ __device__ __forceinline__ void issue_all(const DmaPlan& p, int w) {
     if (j < 4 || w < 4) issue_one(p, w, j);
 }
 
+// fp8 cache: staging slot = latent rows (32 x 512 B) at 0, RoPE rows
+// (32 x 64 B) at 16384, the 32 per-token scales (then repeated) at 18432.
+// 19 wave loads per sub-tile: k < 16 latent rows 2k, 2k+1; k = 16, 17 RoPE
+// rows 16(k-16)..+15; k = 18 the scales (4 bytes per lane).  Wave w issues
+// k = w, w + 8, w + 16: waves 0-2 three loads, waves 3-7 two.
+struct F8Plan {
+  const char* lat;
+  const char* rop;
+  const float* scl;
+  uint32_t voff[3];
+  uint32_t dst;
+};
+
+__device__ __forceinline__ F8Plan plan_sub_f8(const DecodeArgs& a, const TileInfo& t, int hh,
+                                              uint32_t dst, int w, int lane) {
+  const int in_page = min(kTile, t.rem);  // >= 1
+  const int64_t stride = a.row_stride;    // bytes
+  F8Plan p;
+  p.lat = (const char*)a.latent + t.row0 * stride;
+  p.rop = (const char*)a.rope + t.row0 * stride;
+  p.scl = a.kv_scale + t.row0;
+  p.dst = dst;
+#pragma unroll
+  for (int i = 0; i < 3; ++i) {
+    const int k = w + 8 * i;
+    int r, col;
+    if (k < 16) {
+      r = 2 * k + (lane >> 5);
+      col = lane & 31;
+    } else if (k < 18) {
+      r = 16 * (k - 16) + (lane >> 2);
+      col = lane & 3;
+    } else {
+      r = lane & 31;
+      col = 0;
+    }
+    r += 32 * hh;
+    r = r < in_page ? r : in_page - 1;  // past the end: re-read the last row
+    p.voff[i] = k < 18 ? (uint32_t)(r * stride) + (uint32_t)(col * 16) : (uint32_t)(r * 4);
+  }
+  return p;
+}
+
+__device__ __forceinline__ void issue_all_f8(const F8Plan& p, int w) {
+#pragma unroll
+  for (int i = 0; i < 3; ++i) {
+    const int k = w + 8 * i;
+    if (k < 16)
+      lds_dma16(p.lat, p.voff[i], p.dst + (uint32_t)(k * 1024));
+    else if (k < 18)
+      lds_dma16(p.rop, p.voff[i], p.dst + (uint32_t)(k * 1024));
+    else if (k == 18)
+      lds_dma4(p.scl, p.voff[i], p.dst + 18432u);
+  }
+}
+
+// Exact e4m3 -> bf16 conversion of a staged sub-tile into the bf16 tile
+// layout (every e4m3 value is a bf16 value).  512 threads, 2304 chunks of 8.
+__device__ __forceinline__ void convert_f8(const char* stage, char* tile, int tid) {
+#pragma unroll
+  for (int i = 0; i < 5; ++i) {
+    const int c = tid + 512 * i;  // bf16 chunk: row c / 72, 16-byte chunk c % 72
+    if (i < 4 || c < 2304) {
+      const int r = c / 72, kap = c % 72;
+      const uint2 raw = *(const uint2*)(stage + (kap < 64 ? r * 512 + kap * 8
+                                                          : 16384 + r * 64 + (kap - 64) * 8));
+      const f32x2 v0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)raw.x, false);
+      const f32x2 v1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)raw.x, true);
+      const f32x2 v2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)raw.y, false);
+      const f32x2 v3 = __builtin_amdgcn_cvt_pk_f32_fp8((int)raw.y, true);
+      const bf16x8 v = {(__bf16)v0.x, (__bf16)v0.y, (__bf16)v1.x, (__bf16)v1.y,
+                        (__bf16)v2.x, (__bf16)v2.y, (__bf16)v3.x, (__bf16)v3.y};
+      const int cg = kap >> 3, kc = kap & 7, rg = r >> 3, rho = r & 7;
+      const int entry = 8 * (kc ^ (rg & 1)) + (rho ^ (4 * ((kc ^ (kc >> 1)) & 1)));
+      *(bf16x8*)(tile + (cg * 4 + rg) * 1024 + entry * 16) = v;
+    }
+  }
+}
+
 // Per-lane LDS byte offsets of the operand reads.  Each is computed where it
 // is used from an opaque copy of the lane id: a handful of VALU ops, where
 // keeping them live across the loop would cost registers the accumulators
@@ -252,13 +342,16 @@ __device__ __forceinline__ uint32_t off_pr(int lane) {
 
 // Q k-slices held in LDS: rows of 64 B (row 16w + lane%16, chunk lane/16),
 // 16-byte chunk c of row r stored at chunk c ^ ((r >> 1) & 3).
+template <bool F8>
 __device__ __forceinline__ uint32_t off_ql(int lane, int w) {
   const int g = lane >> 4, li = lane & 15;
-  return (uint32_t)(kOffQ + (16 * w + li) * 64 + 16 * (g ^ ((li >> 1) & 3)));
+  return (uint32_t)(Lds<F8>::kOffQ + (16 * w + li) * 64 + 16 * (g ^ ((li >> 1) & 3)));
 }
 
+template <bool F8>
 __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeArgs a) {
-  __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes];
+  using L = Lds<F8>;
+  __shared__ __attribute__((aligned(1024))) char smem[L::kBytes];
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -271,7 +364,7 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeArgs a) {
   const int qi = qk_active ? qrow0 / a.heads : 0;
   const int h0 = qk_active ? qrow0 % a.heads : 0;
   const int u = blockIdx.x;
-  const int my_loads = w < 4 ? 5 : 4;
+  const int my_loads = F8 ? (w < 3 ? 3 : 2) : (w < 4 ? 5 : 4);  // direct loads per sub-tile
 
   int64_t T, unused;
   wave_tile_sums(a.seq_lens, a.batch, 0, T, unused);
@@ -289,21 +382,30 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeArgs a) {
   }
 
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_char*)smem;
-  char* pbuf = smem + kOffP;
-  float* alpha_buf = (float*)(smem + kOffAlpha);
-  float* lbuf = (float*)(smem + kOffL);
-  uint8_t* flags = (uint8_t*)(smem + kOffFlag);
+  char* pbuf = smem + L::kOffP;
+  float* alpha_buf = (float*)(smem + L::kOffAlpha);
+  float* lbuf = (float*)(smem + L::kOffL);
+  uint8_t* flags = (uint8_t*)(smem + L::kOffFlag);
+  // issue the direct loads of (tile x, half hh) into ring slot `sl`
+  auto issue = [&](const TileInfo& t, int hh, int sl, int lane_) {
+    const uint32_t dst = lds0 + (uint32_t)(sl * L::kStage);
+    if constexpr (F8)
+      issue_all_f8(plan_sub_f8(a, t, hh, dst, w, lane_), w);
+    else
+      issue_all(plan_sub(a, t, hh, dst, w, lane_), w);
+  };
   const float sl2 = a.softmax_scale * kLog2e;
 
   // ---- prologue: sub-tiles 0 and 1 of the unit (a unit has >= 1 tile = 2 subs)
   const int64_t nsub = 2 * (x1 - x0);
   int64_t cx = x0, px = x0;  // tile of the sub-tile in use / next to issue
   int chh = 0, phh = 0;      // and its half
-  issue_all(plan_sub(a, tile_info(win, px), phh, lds0, w, lane), w);
+  issue(tile_info(win, px), phh, 0, lane);
   step_sub(px, phh);
-  issue_all(plan_sub(a, tile_info(win, px), phh, lds0 + kSubBytes, w, lane), w);
+  issue(tile_info(win, px), phh, 1, lane);
   step_sub(px, phh);
 
+  constexpr int kQReg = L::kQReg;
   bf16x8 q[kQReg];
   f32x16 o[4][2];
   float m_run = -INFINITY, l_run = 0.f;
@@ -322,7 +424,7 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeArgs a) {
         for (int kk = 0; kk < kQReg; ++kk) q[kk] = qp[4 * kk + g];
 #pragma unroll
         for (int kk = kQReg; kk < 18; ++kk)
-          *(bf16x8*)(smem + off_ql(ln, w) + (kk - kQReg) * 8192) = qp[4 * kk + g];
+          *(bf16x8*)(smem + off_ql<F8>(ln, w) + (kk - kQReg) * 8192) = qp[4 * kk + g];
       }
       wait_vm0();
 #pragma unroll
@@ -341,14 +443,23 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeArgs a) {
       const int s2 = slot + 2 >= kRing ? slot + 2 - kRing : slot + 2;
       if (px >= win.wx + win.wn)  // slide the window to start at the tile in use
         build_window(a, cx, x1, win.b0, win.pb0, ln, win);
-      issue_all(plan_sub(a, tile_info(win, px), phh, lds0 + (uint32_t)(s2 * kSubBytes), w, ln), w);
+      issue(tile_info(win, px), phh, s2, ln);
       step_sub(px, phh);
     }
 
-    const char* tile = smem + slot * kSubBytes;
+    const char* stage = smem + slot * L::kStage;
+    const bool has_tokens = 32 * chh < ci.rem;  // uniform: an empty second half does nothing
+    if constexpr (F8) {
+      if (has_tokens) {  // every wave converts its share, then all may read the tile
+        int tid = (int)threadIdx.x;
+        asm volatile("" : "+v"(tid));  // recompute the addresses, do not keep them live
+        convert_f8(stage, smem + L::kConv, tid);
+        block_sync();
+      }
+    }
+    const char* tile = F8 ? smem + L::kConv : stage;
     char* pb = pbuf;  // one P buffer: the barrier at the top of the next
                       // sub-tile orders its reuse after every wave's reads
-    const bool has_tokens = 32 * chh < ci.rem;  // uniform: an empty second half does nothing
     // visible tokens of this sub-tile: all up to the sequence end, or with
     // the causal mask those up to the query's own position
     int nv = ci.rem - 32 * chh - (a.causal ? a.q_len - 1 - qi : 0);
@@ -363,7 +474,7 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeArgs a) {
         f32x4 s[2] = {f32x4{}, f32x4{}};
         constexpr int kPf = 2;
         const int lq = fresh_lane();
-        const uint32_t o_qk = off_qk(lq), o_ql = off_ql(lq, w);
+        const uint32_t o_qk = off_qk(lq), o_ql = off_ql<F8>(lq, w);
         bf16x8 ka[kPf + 1][2], qb[kPf + 1];
         auto kload = [&](int kk) {
           const int e = kk % (kPf + 1);
@@ -382,6 +493,14 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeArgs a) {
           s[0] = mfma16(ka[e][0], qk, s[0]);
           s[1] = mfma16(ka[e][1], qk, s[1]);
           __builtin_amdgcn_sched_barrier(0);
+        }
+        f32x4 sc[2];  // fp8: the tokens' dequantisation scales
+        if constexpr (F8) {
+          const float* scl = (const float*)(stage + 18432);
+          sc[0] = *(const f32x4*)(scl + 4 * (ln >> 4));
+          sc[1] = *(const f32x4*)(scl + 16 + 4 * (ln >> 4));
+          s[0] *= sc[0];
+          s[1] *= sc[1];
         }
         if (nv < kSub) {  // mask the tokens past the visible end
 #pragma unroll
@@ -414,7 +533,8 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeArgs a) {
           for (int r = 0; r < 4; ++r) {
             const float e = __builtin_amdgcn_exp2f(fmaf(s[j][r], sl2, -m_use));
             l_run += e;
-            pw[4 * j + r] = (__bf16)e;
+            // fp8: the value rows in LDS are unscaled, so P carries the scale
+            pw[4 * j + r] = (__bf16)(F8 ? e * sc[j][r] : e);
           }
       }
       // P rows of this wave's heads (zeros when it has nothing to score)
@@ -511,15 +631,19 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeArgs a) {
 
 bool mfma_decode_supports(const mla_dims_t& d, int64_t row_stride, const void* latent,
                           const void* rope) {
-  return d.q_dtype == MLA_BF16 && d.kv_dtype == MLA_BF16 && d.d_latent == 512 &&
-         d.d_rope == 64 && d.heads % 16 == 0 && (row_stride * 2) % 16 == 0 &&
+  const int64_t row_bytes = row_stride * (d.kv_dtype == MLA_BF16 ? 2 : 1);
+  return d.q_dtype == MLA_BF16 && (d.kv_dtype == MLA_BF16 || d.kv_dtype == MLA_FP8_E4M3) &&
+         d.d_latent == 512 && d.d_rope == 64 && d.heads % 16 == 0 && row_bytes % 16 == 0 &&
          ((uintptr_t)latent & 15) == 0 && ((uintptr_t)rope & 15) == 0;
 }
 
 hipError_t launch_decode_mfma(const mla_dims_t& d, const DecodeArgs& a, hipStream_t s) {
   const int R = d.q_len * d.heads;
   dim3 grid((unsigned)a.num_splits, (unsigned)((R + 127) / 128));
-  hipLaunchKernelGGL(decode_split_kernel, grid, dim3(512), 0, s, a);
+  if (d.kv_dtype == MLA_FP8_E4M3)
+    hipLaunchKernelGGL(decode_split_kernel<true>, grid, dim3(512), 0, s, a);
+  else
+    hipLaunchKernelGGL(decode_split_kernel<false>, grid, dim3(512), 0, s, a);
   return hipGetLastError();
 }
 

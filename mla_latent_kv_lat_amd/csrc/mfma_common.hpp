@@ -10,6 +10,7 @@ namespace mfma {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
@@ -35,6 +36,13 @@ __device__ __forceinline__ bf16x8 cat(bf16x4 a, bf16x4 b) {
 // the compiler's blanket wait before every later LDS read.
 __device__ __forceinline__ void lds_dma16(const void* sbase, uint32_t voff, uint32_t m0) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(m0), "v"(voff),
+               "s"(sbase)
+               : "memory", "m0");
+}
+
+// As lds_dma16 with 4 bytes per lane (256 bytes of LDS per wave).
+__device__ __forceinline__ void lds_dma4(const void* sbase, uint32_t voff, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2" ::"s"(m0), "v"(voff),
                "s"(sbase)
                : "memory", "m0");
 }

@@ -154,6 +154,29 @@ def test_bf16_mfma_matches_generic_kernels():
     assert np.max(np.abs(a["lse"] - b["lse"])) < 1e-2
 
 
+FP8_RAGGED = scaled(CONFIGS["fp8_b128_l16k_q2"], name="fp8_ragged", batch=3, seq_len=0,
+                    len_lo=2, len_hi=700)
+
+
+@pytest.mark.parametrize("paged", [False, True])
+@pytest.mark.parametrize("splits", [1, 7, 300])
+def test_fp8_mfma_ragged_causal(paged, splits):
+    # two causal queries per sequence, the shortest sequence holding just them
+    inp = MLAInputs(scaled(FP8_RAGGED, paged=paged))
+    inp.seq_lens[0] = 2
+    inp.positions[0] = [0, 1]
+    check_all_stages(inp, run_gpu(inp, num_splits=splits))
+
+
+def test_fp8_mfma_matches_generic_kernels():
+    inp = MLAInputs(scaled(FP8_RAGGED, paged=True, seed=77))
+    dev = to_device(inp)
+    a = run_gpu(inp, num_splits=5, dev=dev)
+    b = run_gpu(inp, flags=mla.FLAG_GENERIC, num_splits=5, dev=dev)
+    assert row_rel_err(a["o_lat"], b["o_lat"]) < 2e-2
+    assert np.max(np.abs(a["lse"] - b["lse"])) < 2e-2
+
+
 def test_bf16_mfma_32_heads_and_empty_sequence():
     cfg = scaled(BF16_RAGGED, heads=32, batch=4, len_lo=1, len_hi=200)
     inp = MLAInputs(cfg)
