@@ -140,6 +140,13 @@ def main():
     G = step.num_splits
     stream = torch.cuda.current_stream()
 
+    args_run = dict(q_nope=dev.q_nope, q_rope=dev.q_rope, positions=dev.positions, w_uk=dev.w_uk,
+                    w_uv=dev.w_uv, latent=dev.latent, rope=dev.rope,
+                    kv_row_stride=dev.kv_row_stride, kv_scale=dev.kv_scale,
+                    seq_lens=dev.seq_lens, block_table=dev.block_table,
+                    max_blocks_per_seq=dev.max_blocks_per_seq, max_seq_len=dev.max_seq_len,
+                    causal=dev.causal, softmax_scale=dev.softmax_scale, rope_base=dev.rope_base)
+
     def absorb():
         mla.mla_absorb_q(d, dev.q_nope, dev.q_rope, dev.positions, dev.rope_base, dev.w_uk,
                          step.q_abs, stream)
@@ -159,24 +166,30 @@ def main():
 
     parts = [absorb, decode, combine, out_proj]
 
+    def timed(fn, k):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(k):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / k
+
     for _ in range(args.warmup):
-        for f in parts:
-            f()
+        step.run(**args_run)
     torch.cuda.synchronize()
     if not torch.isfinite(step.o.float()).all():
         raise RuntimeError("non-finite decode output")
 
-    # ---- timed region: exactly K steps
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        for f in parts:
-            f()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    ms_step = ev0.elapsed_time(ev1) / args.steps
+    # ---- eager launches, then the same step replayed from a HIP graph
+    ms_eager = timed(lambda: step.run(**args_run), args.steps)
+    graph = step.capture(**args_run)
+    for _ in range(args.warmup):
+        graph.replay()
+    # ---- timed region: exactly K steps (graph replays on the same stream)
+    ms_step = timed(graph.replay, args.steps)
 
     # ---- per-kernel durations (events around each launch, same stream)
     evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -222,6 +235,7 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5),
         "us_per_step": round(us_step, 2),
+        "eager_us_per_step": round(ms_eager * 1e3, 2),
         "tflops": round(tflops, 2),
         "pct_roofline": round(100.0 * t_roof / (ms_step * 1e-3), 2),
         "higher_is_better": True,
@@ -233,7 +247,8 @@ def main():
                    "cached_tokens": acc["tokens"], "heads": cfg.heads, "q_len": cfg.q_len,
                    "d_latent": cfg.d_latent, "d_rope": cfg.d_rope, "d_nope": cfg.d_nope,
                    "d_v": cfg.d_v, "paged_block": 64 if cfg.paged else 0,
-                   "kv_dtype": cfg.kv_dtype, "num_splits": G, "parallelism": "single GPU"},
+                   "kv_dtype": cfg.kv_dtype, "num_splits": G, "parallelism": "single GPU",
+                   "launch": "HIP graph replay of the four kernels (eager time beside)"},
         "kernels_us": {"absorb_q": round(kern_ms[0] * 1e3, 2), "decode_attn": round(kern_ms[1] * 1e3, 2),
                        "combine": round(kern_ms[2] * 1e3, 2), "out_proj": round(kern_ms[3] * 1e3, 2)},
         "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": PEAK_HBM_GBS,

@@ -30,110 +30,124 @@ using namespace mfma;
 
 // ===================================================================== absorb
 // q_abs[m, h, 0:d_c] = q_nope[m, h, :] W_UK[h]   ([ARCH] 3.1 absorbed query)
-// One wave per (head, 128-column block).  The wave stages its 128 columns of
-// W_UK[h] (d_n rows) in LDS with all loads in flight, then reads them back
-// transposed as the MFMA B operand; q_nope rows are the A operand straight
-// from memory.  The RoPE part (pair k turns by pos * base^(-2k/d_r), angle
-// in fp64) is split over the head's column blocks by rows.
+// One workgroup of 4 waves per (head, 128-column block).  The block of
+// W_UK[h] (d_n rows x 128 columns) is staged in LDS once; each wave then
+// owns 16 query rows of every 64-row block and computes the transposed
+// product q_abs^T = W^T q^T with v_mfma_f32_16x16x32_bf16:
+//   A (16 x 32) = W^T: lane l holds output column l%16, k 8(l/16)..+7,
+//                 read transposed from LDS with ds_read_b64_tr_b16;
+//   B (32 x 16) = q^T: lane l holds query row l%16, k 8(l/16)..+7, one
+//                 16-byte load straight from q_nope;
+//   C (16 x 16): lane l holds row m = l%16, output columns 4(l/16)..+3,
+//                 stored as 8 contiguous bytes.
+// The RoPE part ([ARCH] 2.3: pair k of the query turns by pos * base^(-2k/d_r))
+// is spread over all threads of the head's workgroups: the angle is formed
+// and reduced modulo 2 pi in double precision, then sin/cos in single.
 constexpr int kAbsCols = 128;
 constexpr int kAbsPitch = 320;  // bytes per staged W row: 256 + 64 keeps tr reads conflict-free
 constexpr int kAbsMaxDn = 128;
 
-__global__ __launch_bounds__(64) void absorb_mfma_kernel(
+__global__ __launch_bounds__(256) void absorb_mfma_kernel(
     const uint16_t* __restrict__ q_nope, const uint16_t* __restrict__ q_rope,
     const int32_t* __restrict__ positions, double rope_base, const uint16_t* __restrict__ w_uk,
     uint16_t* __restrict__ q_abs, int M, int H, int d_n, int d_r, int d_c) {
   __shared__ __attribute__((aligned(16))) char wsm[kAbsMaxDn * kAbsPitch];
   const int h = blockIdx.x;
   const int cb = blockIdx.y;
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6;
   const int W = d_c + d_r;
 
-  // stage W_UK[h][:, cb*128 .. +128]: lane reads chunk lane%16 of rows lane/16 + 4i
-  const char* wsrc = (const char*)(w_uk + (int64_t)h * d_n * d_c + cb * kAbsCols);
-  {
-    // rows past d_n re-read the last row and land in LDS rows nobody reads
-    uint4 st[kAbsMaxDn / 4];
+  const int g = lane >> 4, li = lane & 15;
+  const int ksteps = (d_n + 31) / 32;
+  // B operand (q rows m = mb + lane%16, k 8(lane/16).. of each 32-step);
+  // the first block's loads go out together with the W loads below
+  auto load_q = [&](int mb, bf16x8 (&qb)[kAbsMaxDn / 32]) {
+    const int m = mb + li;
 #pragma unroll
-    for (int i = 0; i < kAbsMaxDn / 4; ++i) {
-      const int r = (lane >> 4) + 4 * i;
-      const int rs = r < d_n ? r : d_n - 1;
-      st[i] = *(const uint4*)(wsrc + (int64_t)rs * d_c * 2 + (lane & 15) * 16);
+    for (int ks = 0; ks < kAbsMaxDn / 32; ++ks) {
+      const int k0 = 32 * ks + 8 * g;
+      qb[ks] = (m < M && ks < ksteps && k0 < d_n)
+                   ? *(const bf16x8*)(q_nope + ((int64_t)m * H + h) * d_n + k0)
+                   : bf16x8{};
     }
+  };
+  bf16x8 qb[kAbsMaxDn / 32];
+
+  // stage W_UK[h][:, cb*128 .. +128]: thread reads chunk tid%16 of rows
+  // tid/16 + 16i; rows past d_n are zero (they meet zero-padded k of q)
+  {
+    const char* wsrc = (const char*)(w_uk + (int64_t)h * d_n * d_c + cb * kAbsCols);
+    uint4 st[kAbsMaxDn / 16];
 #pragma unroll
-    for (int i = 0; i < kAbsMaxDn / 4; ++i)
-      *(uint4*)(wsm + ((lane >> 4) + 4 * i) * kAbsPitch + (lane & 15) * 16) = st[i];
+    for (int i = 0; i < kAbsMaxDn / 16; ++i) {
+      const int r = (tid >> 4) + 16 * i;
+      st[i] = r < d_n ? *(const uint4*)(wsrc + (int64_t)r * d_c * 2 + (tid & 15) * 16)
+                      : make_uint4(0, 0, 0, 0);
+    }
+    load_q(16 * w, qb);
+#pragma unroll
+    for (int i = 0; i < kAbsMaxDn / 16; ++i)
+      *(uint4*)(wsm + ((tid >> 4) + 16 * i) * kAbsPitch + (tid & 15) * 16) = st[i];
+  }
+
+  // RoPE pairs of this head, spread over its column-block workgroups
+  const int half = d_r / 2;
+  if (half > 0) {
+    const int stride = (int)gridDim.y * 256;
+    for (int p = cb * 256 + tid; p < M * half; p += stride) {
+      const int m = p / half, k = p % half;
+      const double theta = pow(rope_base, -2.0 * k / d_r);
+      double ang = (double)positions[m] * theta;
+      ang -= 6.283185307179586 * rint(ang * 0.15915494309189535);  // into [-pi, pi]
+      float sn, cs;
+      __sincosf((float)ang, &sn, &cs);
+      const int64_t src = ((int64_t)m * H + h) * d_r + 2 * k;
+      const float x0 = bf16_to_f32(q_rope[src]), x1 = bf16_to_f32(q_rope[src + 1]);
+      const int64_t dst = ((int64_t)m * H + h) * W + d_c + 2 * k;
+      const uint32_t packed = (uint32_t)f32_to_bf16(x0 * cs - x1 * sn) |
+                              ((uint32_t)f32_to_bf16(x0 * sn + x1 * cs) << 16);
+      *(uint32_t*)(q_abs + dst) = packed;
+    }
   }
   __syncthreads();
 
-  const int hf = lane >> 5, n32 = lane & 31;
-  const int li = lane & 15, ch = (lane >> 4) & 1;
-  constexpr int kK = kAbsMaxDn / 16;  // k-steps (rows past d_n are multiplied by zero A)
-  for (int mb = 0; mb < M; mb += 64) {
-    // all A loads of two 32-row blocks in flight at once
-    bf16x8 av[2][kK];
+  for (int mb = 16 * w; mb < M; mb += 64) {
+    const int m = mb + li;
+    const bool mv = m < M;
+    f32x4 acc[8];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int m = mb + 32 * t + n32;
+    for (int nb = 0; nb < 8; ++nb) acc[nb] = f32x4{};
 #pragma unroll
-      for (int k = 0; k < kK; ++k)
-        av[t][k] = (m < M && 16 * k < d_n)
-                       ? *(const bf16x8*)(q_nope + ((int64_t)m * H + h) * d_n + 16 * k + 8 * hf)
-                       : bf16x8{};
-    }
+    for (int ks = 0; ks < kAbsMaxDn / 32; ++ks) {
+      if (ks >= ksteps) break;
+      const int r0 = 32 * ks + 8 * g + (li >> 2);
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      if (mb + 32 * t >= M) break;
-      f32x16 acc[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
-#pragma unroll
-      for (int k = 0; k < kK; ++k) {
-        if (16 * k >= d_n) break;
-        const int r0 = 16 * k + 8 * hf + (li >> 2);
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-          const uint32_t off0 = (uint32_t)(r0 * kAbsPitch + (nb * 32 + 16 * ch + 4 * (li & 3)) * 2);
-          acc[nb] = mfma32(av[t][k], cat(lds_tr4(wsm, off0), lds_tr4(wsm, off0 + 4 * kAbsPitch)), acc[nb]);
-        }
-      }
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int mr = mb + 32 * t + 8 * (r >> 2) + 4 * hf + (r & 3);
-          if (mr < M)
-            q_abs[((int64_t)mr * H + h) * W + cb * kAbsCols + nb * 32 + n32] = f32_to_bf16(acc[nb][r]);
-        }
-    }
-  }
-
-  // RoPE of rows m = cb, cb + nblocks, ... of this head: lane -> (pair k, row
-  // offset); d_r <= 128, so one pass covers 64 / (d_r/2) rows.
-  const int half = d_r / 2;
-  if (half > 0) {
-    const int nblocks = gridDim.y;
-    const int rows_per_pass = 64 / half;
-    const int k = lane % half, rsub = lane / half;
-    if (rsub < rows_per_pass) {
-      const double theta = pow(rope_base, -2.0 * k / d_r);
-      for (int m = cb + rsub * nblocks; m < M; m += rows_per_pass * nblocks) {
-        double sn, cs;
-        sincos((double)positions[m] * theta, &sn, &cs);
-        const int64_t src = ((int64_t)m * H + h) * d_r + 2 * k;
-        const float x0 = bf16_to_f32(q_rope[src]), x1 = bf16_to_f32(q_rope[src + 1]);
-        const int64_t dst = ((int64_t)m * H + h) * W + d_c + 2 * k;
-        q_abs[dst] = f32_to_bf16(x0 * (float)cs - x1 * (float)sn);
-        q_abs[dst + 1] = f32_to_bf16(x0 * (float)sn + x1 * (float)cs);
+      for (int nb = 0; nb < 8; ++nb) {
+        const uint32_t off = (uint32_t)(r0 * kAbsPitch + (nb * 16 + 4 * (li & 3)) * 2);
+        const bf16x8 wa = cat(lds_tr4(wsm, off), lds_tr4(wsm, off + 4 * kAbsPitch));
+        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa, qb[ks], acc[nb], 0, 0, 0);
       }
     }
+    if (mv) {
+      uint16_t* dst = q_abs + ((int64_t)m * H + h) * W + cb * kAbsCols + 4 * g;
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) {
+        const uint2 v = make_uint2((uint32_t)f32_to_bf16(acc[nb][0]) | ((uint32_t)f32_to_bf16(acc[nb][1]) << 16),
+                                   (uint32_t)f32_to_bf16(acc[nb][2]) | ((uint32_t)f32_to_bf16(acc[nb][3]) << 16));
+        *(uint2*)(dst + nb * 16) = v;
+      }
+    }
+    if (mb + 64 < M) load_q(mb + 64, qb);
   }
 }
 
 // =================================================================== out proj
 // o[m, h, v] = sum_c W_UV[h][v][c] o_lat[m, h, c]   ([ARCH] 3.2)
-// One workgroup per head, one wave per 32 output columns.  Both operands have
-// the contracted latent index contiguous in memory, so they load straight
-// into MFMA registers.  Each wave keeps its 32 rows of W_UV[h] in registers
-// (512-wide latent: 32 steps of 16) and reuses them for every 32-row block.
+// One workgroup per (head, 32 query rows), one wave per 32 output columns.
+// Both operands have the contracted latent index contiguous in memory, so
+// they load straight into MFMA registers: the wave's 32 rows of W_UV[h]
+// (512-wide latent: 32 steps of 16) and its 32 rows of o_lat.
 constexpr int kOutMaxDc = 512;
 
 __global__ __launch_bounds__(256) void out_proj_mfma_kernel(
@@ -141,7 +155,9 @@ __global__ __launch_bounds__(256) void out_proj_mfma_kernel(
     uint16_t* __restrict__ o, int M, int H, int d_c, int d_v) {
   const int h = blockIdx.x;
   const int lane = threadIdx.x & 63, hf = lane >> 5, n32 = lane & 31;
-  const int vb = (blockIdx.y * 4 + (threadIdx.x >> 6)) * 32;
+  const int nvg = (d_v / 32 + 3) / 4;  // groups of 4 v-blocks
+  const int vb = ((blockIdx.y % nvg) * 4 + (threadIdx.x >> 6)) * 32;
+  const int mb0 = (blockIdx.y / nvg) * 32;  // this workgroup's 32 query rows
   if (vb >= d_v) return;
   const bf16x8* bp = (const bf16x8*)(w_uv + ((int64_t)h * d_v + vb + n32) * d_c);
   const int nk = d_c / 16;
@@ -149,7 +165,8 @@ __global__ __launch_bounds__(256) void out_proj_mfma_kernel(
   bf16x8 bw[kK];
 #pragma unroll
   for (int k = 0; k < kK; ++k) bw[k] = k < nk ? bp[2 * k + hf] : bf16x8{};
-  for (int mb = 0; mb < M; mb += 32) {
+  {
+    const int mb = mb0;
     const int m = mb + n32;
     const bf16x8* ap = (const bf16x8*)(o_lat + ((int64_t)(m < M ? m : 0) * H + h) * d_c);
     f32x16 acc = f32x16{};
@@ -176,8 +193,9 @@ __global__ __launch_bounds__(256) void out_proj_mfma_kernel(
 // ================================================================= launchers
 
 bool mfma_absorb_supports(const mla_dims_t& d) {
+  // d_rope % 4: q_abs rows then start 8-byte aligned for the vector stores
   return d.q_dtype == MLA_BF16 && d.d_nope % 16 == 0 && d.d_nope <= kAbsMaxDn &&
-         d.d_latent % kAbsCols == 0 && d.d_rope <= 128;
+         d.d_latent % kAbsCols == 0 && d.d_rope % 4 == 0 && d.d_rope <= 128;
 }
 
 hipError_t launch_absorb_mfma(const mla_dims_t& d, const void* q_nope, const void* q_rope,
@@ -185,7 +203,7 @@ hipError_t launch_absorb_mfma(const mla_dims_t& d, const void* q_nope, const voi
                               void* q_abs, hipStream_t s) {
   const int M = d.batch * d.q_len;
   dim3 grid((unsigned)d.heads, (unsigned)(d.d_latent / kAbsCols));
-  hipLaunchKernelGGL(absorb_mfma_kernel, grid, dim3(64), 0, s,
+  hipLaunchKernelGGL(absorb_mfma_kernel, grid, dim3(256), 0, s,
                      (const uint16_t*)q_nope, (const uint16_t*)q_rope, positions,
                      (double)rope_base, (const uint16_t*)w_uk, (uint16_t*)q_abs, M, d.heads,
                      d.d_nope, d.d_rope, d.d_latent);
@@ -200,7 +218,7 @@ bool mfma_out_proj_supports(const mla_dims_t& d) {
 hipError_t launch_out_proj_mfma(const mla_dims_t& d, const void* o_lat, const void* w_uv,
                                 void* o, hipStream_t s) {
   const int M = d.batch * d.q_len;
-  dim3 grid((unsigned)d.heads, (unsigned)((d.d_v / 32 + 3) / 4));
+  dim3 grid((unsigned)d.heads, (unsigned)(((d.d_v / 32 + 3) / 4) * ((M + 31) / 32)));
   hipLaunchKernelGGL(out_proj_mfma_kernel, grid, dim3(256), 0, s, (const uint16_t*)o_lat,
                      (const uint16_t*)w_uv, (uint16_t*)o, M, d.heads, d.d_latent, d.d_v);
   return hipGetLastError();

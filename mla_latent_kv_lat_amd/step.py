@@ -2,7 +2,9 @@
 
 Argument marshalling only: torch allocates the caller-owned outputs and
 split-K workspaces once; ``run`` enqueues mla_absorb_q, mla_decode_attn,
-mla_combine and mla_out_proj on the current stream.
+mla_combine and mla_out_proj on the current stream.  ``capture`` records the
+same four launches in a HIP graph, whose replay skips the per-launch host
+overhead (the library records kernel launches only, no memset nodes).
 """
 
 from __future__ import annotations
@@ -45,3 +47,17 @@ class DecodeStep:
                        self.lse, stream)
         _b.mla_out_proj(d, self.o_lat, w_uv, self.o, stream)
         return self.o
+
+    def capture(self, **kwargs) -> torch.cuda.CUDAGraph:
+        """Record one step of ``run(**kwargs)`` (without ``stream``) in a HIP
+        graph; ``replay()`` re-runs it on the same inputs and buffers."""
+        cur = torch.cuda.current_stream(self.device)
+        side = torch.cuda.Stream(device=self.device)
+        side.wait_stream(cur)
+        with torch.cuda.stream(side):
+            self.run(**kwargs)  # first launches outside the capture
+        cur.wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            self.run(**kwargs)
+        return graph
