@@ -53,15 +53,13 @@
 #include "common.hpp"
 #include "kernels.hpp"
 #include "mfma_common.hpp"
+#include "decode_common.hpp"
 
 namespace mla {
 namespace {
 
 using namespace mfma;
-
-__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
+using namespace dec;
 
 constexpr int kSub = 32;                       // tokens per LDS sub-tile
 constexpr int kSubBytes = kSub * 576 * 2;      // 36864
@@ -87,86 +85,6 @@ struct Lds {
   static constexpr int kOffQ = kOffFlag + 128;
   static constexpr int kBytes = kOffQ + kQLds * 8192;  // bf16 162944, fp8 161664
 };
-
-// Lane-resident descriptors of tiles wx .. wx+wn-1 of a unit's walk over
-// the cache: lane i describes tile wx+i (its sequence, the tokens from the
-// tile's start to the sequence end, and the tile's first cache row).  The hot
-// loop reads them with v_readlane, so no scalar-memory round trip sits on the
-// path from one sub-tile to the next.  Cache rows fit in 32 bits: 2^31 rows
-// of >= 1 KB would exceed any HBM.
-struct TileWin {
-  int64_t wx;      // first tile (uniform)
-  int wn;          // tiles described (uniform, 1..64)
-  int b0;          // sequence of tile wx ...
-  int64_t pb0;     // ... and the global index of its first tile (uniform)
-  int b, rem, row0;  // per lane
-};
-
-struct TileInfo {
-  int b;
-  int rem;       // tokens from the tile's first row to the sequence end (>= 1)
-  int64_t row0;  // first cache row of the tile
-};
-
-__device__ __forceinline__ int64_t readlane64(int64_t v, int i) {
-  const int lo = __builtin_amdgcn_readlane((int)(uint32_t)v, i);
-  const int hi = __builtin_amdgcn_readlane((int)(v >> 32), i);
-  return (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
-}
-
-// Describe tiles wx .. min(wx+64, x1)-1.  (b_s, pb_s): any sequence at or
-// before the one holding tile wx, and the global index of its first tile.
-// Sequence b ends at global tile E_b = sum of tiles of sequences <= b; tile x
-// lies in the first sequence with E_b > x, which is b_s plus the number of
-// sequences from b_s on that end at or before x (empty ones included).
-// Ends with all vector memory drained.
-__device__ void build_window(const DecodeArgs& a, int64_t wx, int64_t x1, int b_s, int64_t pb_s,
-                             int lane, TileWin& win) {
-  const int64_t x = wx + lane;
-  int cnt = 0;
-  int64_t start = pb_s, carry = pb_s;
-  for (int cb = b_s; cb < a.batch; cb += 64) {
-    const int seq = cb + lane;
-    int64_t incl = seq < a.batch ? tiles_of(a.seq_lens[seq]) : 0;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int64_t o = __shfl_up(incl, d, 64);
-      if (lane >= d) incl += o;
-    }
-    const int64_t e = carry + incl;
-    for (int j = 0; j < 64; ++j) {
-      const int64_t ej = readlane64(e, j);
-      if (ej <= x) {
-        ++cnt;
-        start = ej;
-      }
-    }
-    carry = readlane64(e, 63);
-    if (carry > wx + 63) break;
-  }
-  const bool ok = x < x1;  // then b < batch: tile x belongs to a real sequence
-  const int b = b_s + cnt;
-  const int tis = (int)(x - start);
-  const int len = ok ? a.seq_lens[b] : 0;
-  const int page = ok && a.block_table ? a.block_table[(int64_t)b * a.mbps + tis] : 0;
-  win.wx = wx;
-  win.wn = (int)min((int64_t)64, x1 - wx);
-  win.b0 = __builtin_amdgcn_readfirstlane(b);
-  win.pb0 = uniform64(start);
-  win.b = b;
-  win.rem = len - tis * kTile;
-  win.row0 = a.block_table ? page * kTile : (int)((int64_t)b * a.max_seq_len + (int64_t)tis * kTile);
-  wait_vm0();
-}
-
-__device__ __forceinline__ TileInfo tile_info(const TileWin& win, int64_t x) {
-  const int i = (int)(x - win.wx);
-  TileInfo t;
-  t.b = __builtin_amdgcn_readlane(win.b, i);
-  t.rem = __builtin_amdgcn_readlane(win.rem, i);
-  t.row0 = (int64_t)(uint32_t)__builtin_amdgcn_readlane(win.row0, i);
-  return t;
-}
 
 // Next 32-token sub-tile: second half of the tile, or the next tile.
 __device__ __forceinline__ void step_sub(int64_t& x, int& hh) {
@@ -300,16 +218,8 @@ __device__ __forceinline__ void convert_f8(const char* stage, char* tile, int ti
   }
 }
 
-// Per-lane LDS byte offsets of the operand reads.  Each is computed where it
-// is used from an opaque copy of the lane id: a handful of VALU ops, where
-// keeping them live across the loop would cost registers the accumulators
-// need.
-__device__ __forceinline__ int fresh_lane() {
-  int l = (int)(threadIdx.x & 63);
-  asm volatile("" : "+v"(l));
-  return l;
-}
-
+// Per-lane LDS byte offsets of the operand reads, computed where they are
+// used from fresh_lane().
 // Score A operand inside a sub-tile.  Sub-tile blocks of 8 rows x 8 chunks:
 // row rho / chunk kappa of block (cg, rg) at entry
 // 8*(kappa ^ (rg&1)) + (rho ^ 4*((kappa ^ kappa>>1)&1)).
@@ -492,6 +402,8 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeArgs a) {
           s[1] = mfma16(ka[e][1], qk, s[1]);
           __builtin_amdgcn_sched_barrier(0);
         }
+        mfma_settle(s[0]);
+        mfma_settle(s[1]);
         f32x4 sc[2];  // fp8: the tokens' dequantisation scales
         if constexpr (F8) {
           const float* scl = (const float*)(stage + 18432);

@@ -92,5 +92,16 @@ __device__ __forceinline__ void buffer_store_f32(float v, __amdgpu_buffer_rsrc_t
   __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, (int)voff, (int)soff, 0);
 }
 
+
+// Let the last MFMA into `v` finish before VALU code reads it: 24 wait
+// states, more than an 8-pass MFMA result needs.  The compiler's hazard
+// padding is missing when the first read sits behind a branch join, and a
+// read that early sees a stale accumulator.  The in/out operand orders every
+// later use of `v` after the wait.
+template <typename V>
+__device__ __forceinline__ void mfma_settle(V& v) {
+  asm volatile("s_nop 15\n\ts_nop 7" : "+v"(v));
+}
+
 }  // namespace mfma
 }  // namespace mla
