@@ -134,8 +134,11 @@ int mla_absorb_q(const mla_dims_t* dims, const void* q_nope, const void* q_rope,
  *                tiles [floor(u*T/G), floor((u+1)*T/G)) where T is the total
  *                tile count.  Each unit writes one partial per sequence it
  *                touches, into slot u + b.
- *   o_part       [G + B - 1, Lq*H, d_latent] fp32 workspace: normalised
- *                partial latent outputs (row index i*H + h)
+ *   o_part       [G + B - 1, Lq*H, d_latent] workspace: normalised partial
+ *                latent outputs (row index i*H + h), stored as fp32 when
+ *                q_dtype is MLA_F32 and as IEEE fp16 otherwise (the partials
+ *                are weighted averages of cached values, well inside fp16
+ *                range; its 2^-11 rounding is far below the bf16 outputs')
  *   lse_part     [G + B - 1, Lq*H] fp32 workspace: natural-log LSE of each
  *                partial (-inf when the partial saw no token)
  */
@@ -143,7 +146,7 @@ int mla_decode_attn(const mla_dims_t* dims, const void* q_abs, const void* laten
                     const void* rope_cache, int64_t kv_row_stride, const float* kv_scale,
                     const int32_t* seq_lens, const int32_t* block_table,
                     int32_t max_blocks_per_seq, int32_t block_size, int32_t max_seq_len,
-                    int32_t causal, float softmax_scale, int32_t num_splits, float* o_part,
+                    int32_t causal, float softmax_scale, int32_t num_splits, void* o_part,
                     float* lse_part, void* stream);
 
 /*
@@ -159,7 +162,7 @@ int mla_decode_attn(const mla_dims_t* dims, const void* q_abs, const void* laten
  *   lse_out [B, Lq, H] fp32 natural-log LSE, output; may be NULL
  */
 int mla_combine(const mla_dims_t* dims, int32_t num_splits, const int32_t* seq_lens,
-                const float* o_part, const float* lse_part, void* o_lat, float* lse_out,
+                const void* o_part, const float* lse_part, void* o_lat, float* lse_out,
                 void* stream);
 
 /*
@@ -180,6 +183,11 @@ const char* mla_status_string(int status);
 /* Element counts of the two split-K workspaces for `num_splits` units. */
 int mla_workspace_elems(const mla_dims_t* dims, int32_t num_splits, int64_t* o_part_elems,
                         int64_t* lse_part_elems);
+
+/* Byte sizes of the two split-K workspaces (o_part elements are 4 bytes
+ * when q_dtype is MLA_F32, else 2; lse_part elements are 4 bytes). */
+int mla_workspace_bytes(const mla_dims_t* dims, int32_t num_splits, int64_t* o_part_bytes,
+                        int64_t* lse_part_bytes);
 
 /* A good num_splits for `device`: one work unit per compute unit and row
  * group of 128 query rows.  Host-only query of device properties. */

@@ -44,7 +44,7 @@ class MLADims(ctypes.Structure):
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing; build it with "
-                          "`python -m mla_latent_kv_lat_amd.build`")
+                          "`python mla_latent_kv_lat_amd/build.py`")
     lib = ctypes.CDLL(LIB_PATH)
     P, I32, I64, F, VP = (ctypes.POINTER(MLADims), ctypes.c_int32, ctypes.c_int64,
                           ctypes.c_float, ctypes.c_void_p)
@@ -54,6 +54,7 @@ def _load():
         "mla_combine": [P, I32, VP, VP, VP, VP, VP, VP],
         "mla_out_proj": [P, VP, VP, VP, VP],
         "mla_workspace_elems": [P, I32, ctypes.POINTER(I64), ctypes.POINTER(I64)],
+        "mla_workspace_bytes": [P, I32, ctypes.POINTER(I64), ctypes.POINTER(I64)],
         "mla_num_splits_hint": [P, I32, ctypes.POINTER(I32)],
         "mla_split_plan": [I32, VP, I32, VP, VP, VP],
     }
@@ -133,6 +134,13 @@ def mla_workspace_elems(d: MLADims, num_splits: int):
     a, b = ctypes.c_int64(), ctypes.c_int64()
     _check(_lib.mla_workspace_elems(ctypes.byref(d), int(num_splits), ctypes.byref(a),
                                     ctypes.byref(b)), "mla_workspace_elems")
+    return a.value, b.value
+
+
+def mla_workspace_bytes(d: MLADims, num_splits: int):
+    a, b = ctypes.c_int64(), ctypes.c_int64()
+    _check(_lib.mla_workspace_bytes(ctypes.byref(d), int(num_splits), ctypes.byref(a),
+                                    ctypes.byref(b)), "mla_workspace_bytes")
     return a.value, b.value
 
 

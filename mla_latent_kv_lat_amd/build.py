@@ -1,6 +1,8 @@
 """Build libmla.so (HIP kernels + C ABI) for gfx950 with hipcc, in-tree.
 
-    python -m mla_latent_kv_lat_amd.build
+    python mla_latent_kv_lat_amd/build.py
+
+(run it as a script: importing the package loads the library being built).
 
 Each source compiles to an object in parallel, then one shared library is
 linked next to this file.

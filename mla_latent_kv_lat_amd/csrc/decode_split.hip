@@ -508,11 +508,12 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeArgs a) {
               l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
       }
       block_sync();
-      // rows past R fall outside the resource and are dropped
+      // fp16 partial rows of 1 KB; rows past R fall outside the resource
+      // and are dropped
       const int rows_here = min(128, R - rowg);
-      const __amdgpu_buffer_rsrc_t rs =
-          buffer_rsrc(a.o_part + (sl * R + rowg) * 512, (uint32_t)rows_here * 2048u);
-      const uint32_t vo = (uint32_t)((4 * hf * 512 + 64 * w + n32) * 4);
+      const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(
+          (_Float16*)a.o_part + (sl * R + rowg) * 512, (uint32_t)rows_here * 1024u);
+      const uint32_t vo = (uint32_t)((4 * hf * 512 + 64 * w + n32) * 2);
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb) {
         f32x16 inv16;
@@ -525,9 +526,9 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeArgs a) {
         const f32x16 v0 = o[mb][0] * inv16, v1 = o[mb][1] * inv16;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const uint32_t so = (uint32_t)((mb * 32 + 8 * (r >> 2) + (r & 3)) * 2048);
-          buffer_store_f32(v0[r], rs, vo, so);
-          buffer_store_f32(v1[r], rs, vo + 128, so);
+          const uint32_t so = (uint32_t)((mb * 32 + 8 * (r >> 2) + (r & 3)) * 1024);
+          buffer_store_f16(v0[r], rs, vo, so);
+          buffer_store_f16(v1[r], rs, vo + 64, so);
         }
       }
       new_seg = true;

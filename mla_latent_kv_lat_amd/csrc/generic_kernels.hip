@@ -133,11 +133,16 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(DecodeArgs a) {
     }
     const int64_t slot = u + b;
     const float inv = l > 0.f ? 1.f / l : 0.f;
-    float* op = a.o_part + (slot * R + row) * a.d_c;
+    const int64_t ob = (slot * R + row) * a.d_c;
 #pragma unroll
     for (int k = 0; k < kGenMaxC / 64; ++k) {
       const int c = lane + 64 * k;
-      if (c < a.d_c) op[c] = acc[k] * inv;
+      if (c < a.d_c) {
+        if (a.part_f16)
+          ((_Float16*)a.o_part)[ob + c] = (_Float16)(acc[k] * inv);
+        else
+          ((float*)a.o_part)[ob + c] = acc[k] * inv;
+      }
     }
     if (lane == 0) a.lse_part[slot * R + row] = l > 0.f ? m + logf(l) : -INFINITY;
     x = seg_end;

@@ -22,7 +22,8 @@ struct DecodeArgs {
   int causal;
   float softmax_scale;
   int num_splits;
-  float* o_part;
+  void* o_part;            // normalised partials: fp16 if part_f16, else fp32
+  int part_f16;
   float* lse_part;
 };
 
@@ -34,7 +35,7 @@ hipError_t launch_decode_generic(const mla_dims_t& d, const DecodeArgs& a, hipSt
 hipError_t launch_out_proj_generic(const mla_dims_t& d, const void* o_lat, const void* w_uv,
                                    void* o, hipStream_t s);
 hipError_t launch_combine(const mla_dims_t& d, int num_splits, const int32_t* seq_lens,
-                          const float* o_part, const float* lse_part, void* o_lat,
+                          const void* o_part, const float* lse_part, void* o_lat,
                           float* lse_out, hipStream_t s);
 
 // MFMA kernels (bf16 queries and weights, gfx950).

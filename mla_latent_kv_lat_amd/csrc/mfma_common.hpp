@@ -92,6 +92,12 @@ __device__ __forceinline__ void buffer_store_f32(float v, __amdgpu_buffer_rsrc_t
   __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, (int)voff, (int)soff, 0);
 }
 
+__device__ __forceinline__ void buffer_store_f16(float v, __amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                                 uint32_t soff) {
+  const _Float16 h = (_Float16)v;
+  __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, h), r, (int)voff, (int)soff, 0);
+}
+
 
 // Let the last MFMA into `v` finish before VALU code reads it: 24 wait
 // states, more than an 8-pass MFMA result needs.  The compiler's hazard

@@ -72,7 +72,7 @@ int mla_decode_attn(const mla_dims_t* dims, const void* q_abs, const void* laten
                     const void* rope_cache, int64_t kv_row_stride, const float* kv_scale,
                     const int32_t* seq_lens, const int32_t* block_table,
                     int32_t max_blocks_per_seq, int32_t block_size, int32_t max_seq_len,
-                    int32_t causal, float softmax_scale, int32_t num_splits, float* o_part,
+                    int32_t causal, float softmax_scale, int32_t num_splits, void* o_part,
                     float* lse_part, void* stream) {
   int st = check_dims(dims);
   if (st) return st;
@@ -110,6 +110,7 @@ int mla_decode_attn(const mla_dims_t* dims, const void* q_abs, const void* laten
   a.softmax_scale = softmax_scale;
   a.num_splits = num_splits;
   a.o_part = o_part;
+  a.part_f16 = dims->q_dtype != MLA_F32;
   a.lse_part = lse_part;
   hipStream_t s = (hipStream_t)stream;
   (void)hipGetLastError();
@@ -120,7 +121,7 @@ int mla_decode_attn(const mla_dims_t* dims, const void* q_abs, const void* laten
 }
 
 int mla_combine(const mla_dims_t* dims, int32_t num_splits, const int32_t* seq_lens,
-                const float* o_part, const float* lse_part, void* o_lat, float* lse_out,
+                const void* o_part, const float* lse_part, void* o_lat, float* lse_out,
                 void* stream) {
   int st = check_dims(dims);
   if (st) return st;
@@ -158,6 +159,17 @@ int mla_workspace_elems(const mla_dims_t* dims, int32_t num_splits, int64_t* o_p
   const int64_t rows = (int64_t)dims->q_len * dims->heads;
   *o_part_elems = slots * rows * dims->d_latent;
   *lse_part_elems = slots * rows;
+  return MLA_OK;
+}
+
+int mla_workspace_bytes(const mla_dims_t* dims, int32_t num_splits, int64_t* o_part_bytes,
+                        int64_t* lse_part_bytes) {
+  if (!o_part_bytes || !lse_part_bytes) return MLA_ERR_INVALID_ARG;
+  int64_t no = 0, nl = 0;
+  const int st = mla_workspace_elems(dims, num_splits, &no, &nl);
+  if (st) return st;
+  *o_part_bytes = no * (dims->q_dtype == MLA_F32 ? 4 : 2);
+  *lse_part_bytes = nl * 4;
   return MLA_OK;
 }
 

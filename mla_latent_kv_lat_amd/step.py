@@ -28,7 +28,9 @@ class DecodeStep:
         n_o, n_l = _b.mla_workspace_elems(d, self.num_splits)
         kw = dict(device=self.device)
         self.q_abs = torch.empty((B, Lq, H, W), dtype=qt, **kw)
-        self.o_part = torch.empty(max(n_o, 1), dtype=torch.float32, **kw)
+        # normalised partials: fp32 on the fp32 path, fp16 otherwise (mla.h)
+        pt = torch.float32 if d.q_dtype == _b.F32 else torch.float16
+        self.o_part = torch.empty(max(n_o, 1), dtype=pt, **kw)
         self.lse_part = torch.empty(max(n_l, 1), dtype=torch.float32, **kw)
         self.o_lat = torch.empty((B, Lq, H, d.d_latent), dtype=qt, **kw)
         self.lse = torch.empty((B, Lq, H), dtype=torch.float32, **kw)

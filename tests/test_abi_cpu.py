@@ -109,6 +109,15 @@ def test_workspace_elems():
     assert l == (128 + 64 - 1) * 256 and o == l * 512
 
 
+@pytest.mark.parametrize("q_dtype,o_bytes", [(mla.BF16, 2), (mla.F32, 4)])
+def test_workspace_bytes(q_dtype, o_bytes):
+    # fp16 partials except on the fp32 path; LSEs always fp32
+    d = _d(batch=5, q_len=1, q_dtype=q_dtype, kv_dtype=q_dtype)
+    o, l = mla.mla_workspace_elems(d, 7)
+    ob, lb = mla.mla_workspace_bytes(d, 7)
+    assert ob == o * o_bytes and lb == l * 4
+
+
 @pytest.mark.parametrize("seed", range(20))
 def test_split_plan_is_a_partition(seed):
     rng = np.random.default_rng(seed)
