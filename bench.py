@@ -5,8 +5,9 @@
 
 A step is the whole hot path on one batch of synthetic inputs already
 resident in GPU memory: mla_absorb_q (W_UK absorption + query RoPE),
-mla_decode_attn (split-K attention over the shared latent cache),
-mla_combine (log-sum-exp merge) and mla_out_proj (W_UV), all on one stream.
+mla_decode_attn (split-K attention over the shared latent cache) and
+mla_combine_out_proj (log-sum-exp merge and W_UV projection in one kernel),
+all on one stream.
 The default workload is DeepSeek-V3 shaped: batch 64, 8192 cached tokens per
 sequence, 128 heads, latent 512 + RoPE 64, bf16, paged in 64-token blocks.
 
@@ -136,7 +137,7 @@ def main():
     DT = {"f32": mla.F32, "bf16": mla.BF16, "fp8": mla.FP8_E4M3}
     d = mla.dims(cfg.batch, cfg.q_len, cfg.heads, cfg.d_nope, cfg.d_rope, cfg.d_latent, cfg.d_v,
                  DT[cfg.q_dtype], DT[cfg.kv_dtype])
-    step = mla.DecodeStep(d, num_splits=args.num_splits or None)
+    step = mla.DecodeStep(d, num_splits=args.num_splits or None, keep_o_lat=False)
     G = step.num_splits
     stream = torch.cuda.current_stream()
 
@@ -157,14 +158,11 @@ def main():
                             mla.TILE_TOKENS, dev.max_seq_len, dev.causal, dev.softmax_scale, G,
                             step.o_part, step.lse_part, stream)
 
-    def combine():
-        mla.mla_combine(d, G, dev.seq_lens, step.o_part, step.lse_part, step.o_lat, step.lse,
-                        stream)
+    def combine_out_proj():
+        mla.mla_combine_out_proj(d, G, dev.seq_lens, step.o_part, step.lse_part, dev.w_uv, step.o,
+                                 step.lse, None, stream)
 
-    def out_proj():
-        mla.mla_out_proj(d, step.o_lat, dev.w_uv, step.o, stream)
-
-    parts = [absorb, decode, combine, out_proj]
+    parts = [absorb, decode, combine_out_proj]
 
     def timed(fn, k):
         e0 = torch.cuda.Event(enable_timing=True)
@@ -248,9 +246,9 @@ def main():
                    "d_latent": cfg.d_latent, "d_rope": cfg.d_rope, "d_nope": cfg.d_nope,
                    "d_v": cfg.d_v, "paged_block": 64 if cfg.paged else 0,
                    "kv_dtype": cfg.kv_dtype, "num_splits": G, "parallelism": "single GPU",
-                   "launch": "HIP graph replay of the four kernels (eager time beside)"},
+                   "launch": "HIP graph replay of the three kernels (eager time beside)"},
         "kernels_us": {"absorb_q": round(kern_ms[0] * 1e3, 2), "decode_attn": round(kern_ms[1] * 1e3, 2),
-                       "combine": round(kern_ms[2] * 1e3, 2), "out_proj": round(kern_ms[3] * 1e3, 2)},
+                       "combine_out_proj": round(kern_ms[2] * 1e3, 2)},
         "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(dec_gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
                      "kernel": "decode_split_kernel",

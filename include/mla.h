@@ -10,6 +10,8 @@
  *   mla_combine      log-sum-exp merge of the partials -> o_lat
  *   mla_out_proj     o = W_UV o_lat                                per head
  *
+ * or as three, with mla_combine_out_proj doing the last two in one launch.
+ *
  * Uncompressed per-head keys and values are never written to memory.
  *
  * Pages cited (title, section):
@@ -176,6 +178,26 @@ int mla_combine(const mla_dims_t* dims, int32_t num_splits, const int32_t* seq_l
  */
 int mla_out_proj(const mla_dims_t* dims, const void* o_lat, const void* w_uv, void* o,
                  void* stream);
+
+/*
+ * mla_combine_out_proj -- mla_combine and mla_out_proj in one call.
+ *
+ * Same results as mla_combine followed by mla_out_proj.  For bf16 queries,
+ * d_latent 512 and d_v % 32 == 0 (without MLA_FLAG_GENERIC) one kernel
+ * merges the partials of 32 query rows of a head in on-chip memory and
+ * projects them right away, so the latent output makes no round trip
+ * through device memory; o_lat may then be NULL (not written).  Otherwise
+ * the two kernels run in turn and o_lat must be given.
+ *
+ *   num_splits, seq_lens, o_part, lse_part: as passed to mla_decode_attn
+ *   w_uv    [H, d_v, d_latent] q_dtype
+ *   o       [B, Lq, H, d_v] q_dtype, output
+ *   lse_out [B, Lq, H] fp32 natural-log LSE, output; may be NULL
+ *   o_lat   [B, Lq, H, d_latent] q_dtype, output; may be NULL (see above)
+ */
+int mla_combine_out_proj(const mla_dims_t* dims, int32_t num_splits, const int32_t* seq_lens,
+                         const void* o_part, const float* lse_part, const void* w_uv, void* o,
+                         float* lse_out, void* o_lat, void* stream);
 
 /* Human-readable name of a status code (static storage). */
 const char* mla_status_string(int status);

@@ -6,13 +6,13 @@ runs the four calls of one decode step on caller-owned torch tensors.
 """
 
 from .binding import (BF16, F32, FLAG_GENERIC, FP8_E4M3, TILE_TOKENS, MLADims, MLAError, dims,
-                      mla_absorb_q, mla_combine, mla_decode_attn, mla_num_splits_hint,
+                      mla_absorb_q, mla_combine, mla_combine_out_proj, mla_decode_attn, mla_num_splits_hint,
                       mla_out_proj, mla_split_plan, mla_workspace_bytes,
                       mla_workspace_elems)
 from .step import DecodeStep
 
 __all__ = [
     "BF16", "F32", "FLAG_GENERIC", "FP8_E4M3", "TILE_TOKENS", "MLADims", "MLAError", "dims",
-    "mla_absorb_q", "mla_combine", "mla_decode_attn", "mla_num_splits_hint", "mla_out_proj",
+    "mla_absorb_q", "mla_combine", "mla_combine_out_proj", "mla_decode_attn", "mla_num_splits_hint", "mla_out_proj",
     "mla_split_plan", "mla_workspace_bytes", "mla_workspace_elems", "DecodeStep",
 ]

@@ -53,6 +53,7 @@ def _load():
         "mla_decode_attn": [P, VP, VP, VP, I64, VP, VP, VP, I32, I32, I32, I32, F, I32, VP, VP, VP],
         "mla_combine": [P, I32, VP, VP, VP, VP, VP, VP],
         "mla_out_proj": [P, VP, VP, VP, VP],
+        "mla_combine_out_proj": [P, I32, VP, VP, VP, VP, VP, VP, VP, VP],
         "mla_workspace_elems": [P, I32, ctypes.POINTER(I64), ctypes.POINTER(I64)],
         "mla_workspace_bytes": [P, I32, ctypes.POINTER(I64), ctypes.POINTER(I64)],
         "mla_num_splits_hint": [P, I32, ctypes.POINTER(I32)],
@@ -128,6 +129,14 @@ def mla_combine(d: MLADims, num_splits, seq_lens, o_part, lse_part, o_lat, lse_o
 def mla_out_proj(d: MLADims, o_lat, w_uv, o, stream=None):
     _check(_lib.mla_out_proj(ctypes.byref(d), _ptr(o_lat), _ptr(w_uv), _ptr(o), _stream(stream)),
            "mla_out_proj")
+
+
+def mla_combine_out_proj(d: MLADims, num_splits, seq_lens, o_part, lse_part, w_uv, o,
+                         lse_out=None, o_lat=None, stream=None):
+    _check(_lib.mla_combine_out_proj(ctypes.byref(d), int(num_splits), _ptr(seq_lens),
+                                     _ptr(o_part), _ptr(lse_part), _ptr(w_uv), _ptr(o),
+                                     _ptr(lse_out), _ptr(o_lat), _stream(stream)),
+           "mla_combine_out_proj")
 
 
 def mla_workspace_elems(d: MLADims, num_splits: int):

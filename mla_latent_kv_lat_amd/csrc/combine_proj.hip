@@ -1,0 +1,265 @@
+// Fused log-sum-exp combine and W_UV projection for gfx950 (bf16 queries,
+// fp16 partials, latent 512).
+//
+// Pages cited (title, section):
+//   [ARCH] "Model Architecture Driving Inference Systems: From MHA/GQA to
+//          DeepSeek MLA Matrix Absorption and Memory Minimalism"
+//   [MATH] "Multi-Head Latent Attention (MLA): Mathematical Foundations, ..."
+//
+// One workgroup of 8 waves per (head h, 32 query rows m = (b, i)); wave w
+// owns rows w, w + 8, w + 16, w + 24 in phases 0-1:
+//   phase 0  the split-K units that touched each row's sequence b (from one
+//            prefix pass over seq_lens per workgroup) and the log-sum-exp of
+//            their partials, lse = log sum_u exp(lse_u); lane k of the wave
+//            keeps the weight exp(lse_u - lse) of the row's k-th unit;
+//   phase 1  o_lat = sum_u exp(lse_u - lse) o_u ([MATH] value absorption:
+//            softmax weights on the cached latents), rounded to bf16 into an
+//            LDS tile (and to memory when asked for).  The partial loads of
+//            all four rows are issued together with their LSE loads, so a
+//            row spanning up to kCPChunk units costs one memory round trip;
+//   phase 2  o = o_lat W_UV[h]^T on v_mfma_f32_32x32x16_bf16 ([ARCH] 3.2):
+//            wave w takes the 32 v-columns 32 (w & 3) + 128 j and half w >> 2
+//            of the 512 latent columns, with its rows of W_UV[h] loaded into
+//            registers at the start; the two halves meet in LDS.
+// The latent output never makes an HBM round trip between the two steps.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "common.hpp"
+#include "kernels.hpp"
+#include "mfma_common.hpp"
+
+namespace mla {
+namespace {
+
+using namespace mfma;
+
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+
+constexpr int kCPRows = 32;
+constexpr int kCPWaves = 8;
+constexpr int kCPRowsPerWave = kCPRows / kCPWaves;
+constexpr int kCPPitch = 1040;  // bytes per bf16 o_lat row in LDS: 1024 + 16 (conflict-free A reads)
+constexpr int kCPChunk = 4;     // partials per row loaded per pass
+
+__device__ inline float lane_value(float v, int k) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), k));
+}
+
+__global__ __launch_bounds__(512) void combine_proj_kernel(
+    int B, int Lq, int H, int G, const int32_t* __restrict__ seq_lens,
+    const _Float16* __restrict__ o_part, const float* __restrict__ lse_part,
+    const uint16_t* __restrict__ w_uv, int d_v, uint16_t* __restrict__ o,
+    float* __restrict__ lse_out, uint16_t* __restrict__ o_lat) {
+  __shared__ __attribute__((aligned(16))) char lat[kCPRows * kCPPitch];
+  __shared__ __attribute__((aligned(16))) float red[4 * 64 * 16];
+  __shared__ int64_t seq_pb[kCPRows], seq_tb[kCPRows];
+  __shared__ int64_t tot_T;
+
+  const int h = blockIdx.x;
+  const int M = B * Lq, R = Lq * H;
+  const int mb0 = blockIdx.y * kCPRows;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int cq = w & 3, kh = w >> 2;
+  const int hf = lane >> 5, n32 = lane & 31;
+
+  // W_UV[h] rows 32 cq + n32, latent half kh: in flight during phases 0-1
+  bf16x8 bw[16];
+  {
+    const int vb = 32 * cq;
+    const bf16x8* bp = (const bf16x8*)(w_uv + ((int64_t)h * d_v + (vb < d_v ? vb : 0) + n32) * 512);
+#pragma unroll
+    for (int k = 0; k < 16; ++k) bw[k] = bp[2 * (16 * kh + k) + hf];
+  }
+
+  // ---- phase 0a: total tiles T and the first tile / tile count of each
+  // sequence the rows touch (at most 32), by wave 0
+  const int b_lo = mb0 / Lq;
+  const int nb = mb0 < M ? (min(M, mb0 + kCPRows) - 1) / Lq - b_lo + 1 : 0;
+  if (w == 0) {
+    int64_t tot = 0, before = 0;
+#pragma unroll 4
+    for (int bb = lane; bb < B; bb += 64) {
+      const int64_t t = tiles_of(seq_lens[bb]);
+      tot += t;
+      before += bb < b_lo ? t : 0;
+    }
+    const int64_t mine = lane < nb ? tiles_of(seq_lens[b_lo + lane]) : 0;
+    int64_t incl = mine;
+#pragma unroll
+    for (int d = 1; d < 32; d <<= 1) {
+      const int64_t x = __shfl_up(incl, d, 64);
+      if (lane >= d) incl += x;
+    }
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) {
+      tot += __shfl_xor(tot, d, 64);
+      before += __shfl_xor(before, d, 64);
+    }
+    if (lane < nb) {
+      seq_pb[lane] = before + incl - mine;
+      seq_tb[lane] = mine;
+    }
+    if (lane == 0) tot_T = tot;
+  }
+  __syncthreads();
+  const int64_t T = tot_T;
+
+  // ---- phase 0b: per row, the units and all first loads (clamped in range;
+  // what an empty unit holds is never used)
+  const int c = 8 * lane;  // latent columns of this lane in phase 1
+  int64_t u0[kCPRowsPerWave], slot0[kCPRowsPerWave];  // slot0 = (u0 + b) R + r
+  int n[kCPRowsPerWave];
+  float lv[kCPRowsPerWave];
+  h8 v[kCPRowsPerWave][kCPChunk];
+#pragma unroll
+  for (int i = 0; i < kCPRowsPerWave; ++i) {
+    const int m = mb0 + w + kCPWaves * i;
+    u0[i] = 0;
+    n[i] = 0;
+    int b = 0, r = h;
+    if (m < M) {
+      b = m / Lq;
+      r = (m % Lq) * H + h;
+      const int64_t pb = seq_pb[b - b_lo], tb = seq_tb[b - b_lo];
+      if (tb > 0) {
+        u0[i] = unit_of_tile(pb, T, G);
+        n[i] = (int)(unit_of_tile(pb + tb - 1, T, G) - u0[i] + 1);
+      }
+    }
+    slot0[i] = (u0[i] + b) * R + r;
+    lv[i] = lse_part[slot0[i] + (int64_t)(lane < n[i] ? lane : 0) * R];
+#pragma unroll
+    for (int k = 0; k < kCPChunk; ++k)
+      v[i][k] = *(const h8*)(o_part + (slot0[i] + (int64_t)(k < n[i] ? k : 0) * R) * 512 + c);
+  }
+
+  // ---- phase 0c / 1: LSE, weights, weighted sum of the partials
+#pragma unroll
+  for (int i = 0; i < kCPRowsPerWave; ++i) {
+    const int j = w + kCPWaves * i, m = mb0 + j;
+    const int ni = n[i];
+    // empty units wrote no partial (weight 0); a row may span more than 64 units
+    const bool ne = lane < ni && unit_begin(u0[i] + lane, T, G) < unit_begin(u0[i] + lane + 1, T, G);
+    const float x = ne ? lv[i] : -INFINITY;
+    float mx = x;
+    for (int k = lane + 64; k < ni; k += 64)
+      if (unit_begin(u0[i] + k, T, G) < unit_begin(u0[i] + k + 1, T, G))
+        mx = fmaxf(mx, lse_part[slot0[i] + (int64_t)k * R]);
+    mx = wave_max(mx);
+    float z = (mx != -INFINITY && x != -INFINITY) ? expf(x - mx) : 0.f;
+    if (mx != -INFINITY)
+      for (int k = lane + 64; k < ni; k += 64)
+        if (unit_begin(u0[i] + k, T, G) < unit_begin(u0[i] + k + 1, T, G))
+          z += expf(lse_part[slot0[i] + (int64_t)k * R] - mx);
+    z = wave_sum(z);
+    const float lse = mx == -INFINITY ? -INFINITY : mx + logf(z);
+    const float wt = (lse != -INFINITY && x != -INFINITY) ? expf(x - lse) : 0.f;
+    if (lse_out && m < M && lane == 0) lse_out[(int64_t)m * H + h] = lse;
+
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+#pragma unroll
+    for (int k = 0; k < kCPChunk; ++k) {
+      const float wk = k < ni ? lane_value(wt, k) : 0.f;
+      if (wk != 0.f)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = fmaf(wk, (float)v[i][k][e], acc[e]);
+    }
+    for (int k0 = kCPChunk; k0 < ni; k0 += kCPChunk) {  // rows spanning more units
+      h8 vv[kCPChunk];
+      float wv[kCPChunk];
+#pragma unroll
+      for (int k = 0; k < kCPChunk; ++k) {
+        const int kk = k0 + k;
+        float wk = 0.f;
+        if (kk < ni) {
+          if (kk < 64) {
+            wk = lane_value(wt, kk);
+          } else if (lse != -INFINITY &&
+                     unit_begin(u0[i] + kk, T, G) < unit_begin(u0[i] + kk + 1, T, G)) {
+            wk = expf(lse_part[slot0[i] + (int64_t)kk * R] - lse);
+          }
+        }
+        wv[k] = wk;
+        vv[k] = wk != 0.f ? *(const h8*)(o_part + (slot0[i] + (int64_t)kk * R) * 512 + c) : h8{};
+      }
+#pragma unroll
+      for (int k = 0; k < kCPChunk; ++k)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = fmaf(wv[k], (float)vv[k][e], acc[e]);
+    }
+    bf16x8 ov;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ov[e] = (__bf16)acc[e];
+    *(bf16x8*)(lat + j * kCPPitch + 16 * lane) = ov;  // rows past M hold zeros
+    if (o_lat && m < M) *(bf16x8*)(o_lat + ((int64_t)m * H + h) * 512 + c) = ov;
+  }
+  __syncthreads();
+
+  // ---- phase 2: o[m, h, vb..vb+31] = o_lat[m] W_UV[h][vb..]^T; the wave sums
+  // latent half kh, half 1 hands its sums to half 0 through LDS
+  const int nvb = d_v / 32;
+  for (int base = 0; base < nvb; base += 4) {
+    const int cb = base + cq;
+    const bool act = cb < nvb;
+    if (base > 0 && act) {
+      const bf16x8* bp = (const bf16x8*)(w_uv + ((int64_t)h * d_v + 32 * cb + n32) * 512);
+#pragma unroll
+      for (int k = 0; k < 16; ++k) bw[k] = bp[2 * (16 * kh + k) + hf];
+    }
+    f32x16 acc2[2] = {f32x16{}, f32x16{}};  // even / odd k-steps: two chains
+    if (act) {
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const bf16x8 av =
+            *(const bf16x8*)(lat + n32 * kCPPitch + (16 * (16 * kh + k) + 8 * hf) * 2);
+        acc2[k & 1] = mfma32(av, bw[k], acc2[k & 1]);
+      }
+    }
+    mfma_settle(acc2[0]);
+    mfma_settle(acc2[1]);
+    f32x16 acc = acc2[0] + acc2[1];
+    f32x4* rp = (f32x4*)(red + (cq * 64 + lane) * 16);
+    if (kh == 1 && act)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) rp[q] = f32x4{acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
+    __syncthreads();
+    if (kh == 0 && act) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 t = rp[q];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[4 * q + e] += t[e];
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int mr = mb0 + 8 * (r >> 2) + 4 * hf + (r & 3);
+        if (mr < M) o[((int64_t)mr * H + h) * d_v + 32 * cb + n32] = f32_to_bf16(acc[r]);
+      }
+    }
+    __syncthreads();
+  }
+}
+
+}  // namespace
+
+bool combine_proj_supports(const mla_dims_t& d) {
+  return d.q_dtype == MLA_BF16 && d.d_latent == 512 && d.d_v % 32 == 0;
+}
+
+hipError_t launch_combine_proj(const mla_dims_t& d, int num_splits, const int32_t* seq_lens,
+                               const void* o_part, const float* lse_part, const void* w_uv,
+                               void* o, float* lse_out, void* o_lat, hipStream_t s) {
+  const int M = d.batch * d.q_len;
+  dim3 grid((unsigned)d.heads, (unsigned)((M + kCPRows - 1) / kCPRows));
+  hipLaunchKernelGGL(combine_proj_kernel, grid, dim3(512), 0, s, d.batch, d.q_len, d.heads,
+                     num_splits, seq_lens, (const _Float16*)o_part, lse_part,
+                     (const uint16_t*)w_uv, d.d_v, (uint16_t*)o, lse_out, (uint16_t*)o_lat);
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -47,6 +47,10 @@ bool mfma_decode_supports(const mla_dims_t& d, int64_t row_stride, const void* l
                           const void* rope);
 hipError_t launch_decode_mfma(const mla_dims_t& d, const DecodeArgs& a, hipStream_t s);
 bool mfma_out_proj_supports(const mla_dims_t& d);
+bool combine_proj_supports(const mla_dims_t& d);
+hipError_t launch_combine_proj(const mla_dims_t& d, int num_splits, const int32_t* seq_lens,
+                               const void* o_part, const float* lse_part, const void* w_uv,
+                               void* o, float* lse_out, void* o_lat, hipStream_t s);
 hipError_t launch_out_proj_mfma(const mla_dims_t& d, const void* o_lat, const void* w_uv,
                                 void* o, hipStream_t s);
 

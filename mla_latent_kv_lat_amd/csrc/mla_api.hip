@@ -149,6 +149,31 @@ int mla_out_proj(const mla_dims_t* dims, const void* o_lat, const void* w_uv, vo
   return launched(launch_out_proj_generic(*dims, o_lat, w_uv, o, s));
 }
 
+int mla_combine_out_proj(const mla_dims_t* dims, int32_t num_splits, const int32_t* seq_lens,
+                         const void* o_part, const float* lse_part, const void* w_uv, void* o,
+                         float* lse_out, void* o_lat, void* stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (dims->batch == 0) return MLA_OK;
+  if (!seq_lens || !w_uv || !o) return MLA_ERR_INVALID_ARG;
+  if (!o_part || !lse_part) return MLA_ERR_WORKSPACE;
+  if (num_splits < 1 || num_splits > 65536) return MLA_ERR_INVALID_ARG;
+  if (!aligned16(o_part) || !aligned16(w_uv) || !aligned16(o) || !aligned16(o_lat))
+    return MLA_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  (void)hipGetLastError();
+  if (use_mfma(dims) && combine_proj_supports(*dims))
+    return launched(launch_combine_proj(*dims, num_splits, seq_lens, o_part, lse_part, w_uv, o,
+                                        lse_out, o_lat, s));
+  // the two kernels in turn: the latent output goes through o_lat
+  if (!o_lat) return MLA_ERR_INVALID_ARG;
+  st = launched(launch_combine(*dims, num_splits, seq_lens, o_part, lse_part, o_lat, lse_out, s));
+  if (st) return st;
+  if (use_mfma(dims) && mfma_out_proj_supports(*dims))
+    return launched(launch_out_proj_mfma(*dims, o_lat, w_uv, o, s));
+  return launched(launch_out_proj_generic(*dims, o_lat, w_uv, o, s));
+}
+
 int mla_workspace_elems(const mla_dims_t* dims, int32_t num_splits, int64_t* o_part_elems,
                         int64_t* lse_part_elems) {
   int st = check_dims(dims);

@@ -1,9 +1,10 @@
-"""One decode step: buffers and the four library calls in order.
+"""One decode step: buffers and the library calls in order.
 
 Argument marshalling only: torch allocates the caller-owned outputs and
-split-K workspaces once; ``run`` enqueues mla_absorb_q, mla_decode_attn,
-mla_combine and mla_out_proj on the current stream.  ``capture`` records the
-same four launches in a HIP graph, whose replay skips the per-launch host
+split-K workspaces once; ``run`` enqueues mla_absorb_q, mla_decode_attn and
+mla_combine_out_proj (the combine and the W_UV projection in one call) on the
+current stream.  ``capture`` records the
+same three launches in a HIP graph, whose replay skips the per-launch host
 overhead (the library records kernel launches only, no memset nodes).
 """
 
@@ -17,8 +18,10 @@ TORCH_DTYPE = {_b.F32: torch.float32, _b.BF16: torch.bfloat16}
 
 
 class DecodeStep:
-    def __init__(self, d: _b.MLADims, *, num_splits: int | None = None, device="cuda"):
+    def __init__(self, d: _b.MLADims, *, num_splits: int | None = None, device="cuda",
+                 keep_o_lat: bool = True):
         self.d = d
+        self.keep_o_lat = keep_o_lat  # also write the latent output o_lat
         self.device = torch.device(device)
         self.num_splits = int(num_splits) if num_splits else _b.mla_num_splits_hint(
             d, self.device.index or 0)
@@ -45,9 +48,12 @@ class DecodeStep:
                            block_table, max_blocks_per_seq, _b.TILE_TOKENS, max_seq_len,
                            causal, softmax_scale, self.num_splits, self.o_part, self.lse_part,
                            stream)
-        _b.mla_combine(d, self.num_splits, seq_lens, self.o_part, self.lse_part, self.o_lat,
-                       self.lse, stream)
-        _b.mla_out_proj(d, self.o_lat, w_uv, self.o, stream)
+        # o_lat may be skipped only where the combine and projection run fused
+        fused = (d.q_dtype == _b.BF16 and d.d_latent == 512 and d.d_v % 32 == 0
+                 and not d.flags & _b.FLAG_GENERIC)
+        _b.mla_combine_out_proj(d, self.num_splits, seq_lens, self.o_part, self.lse_part, w_uv,
+                                self.o, self.lse,
+                                self.o_lat if (self.keep_o_lat or not fused) else None, stream)
         return self.o
 
     def capture(self, **kwargs) -> torch.cuda.CUDAGraph:

@@ -1,6 +1,6 @@
 """A decode step recorded in a HIP graph replays to the eager result.
 
-The graph holds the four kernel launches of one step.  It is replayed three
+The graph holds the kernel launches of one step.  It is replayed three
 times; before each replay the outputs are cleared and an unrelated eager step
 runs on other buffers, and every replay must reproduce the eager outputs
 bit for bit (the kernels are deterministic).

@@ -188,3 +188,39 @@ def test_bf16_mfma_32_heads_and_empty_sequence():
     ref = mla_decode(inp, rows=rows)
     for b in (0, 2, 3):
         assert row_rel_err(out["o"][b], ref["o"][b]) < 2e-2
+
+
+# ------------------------------------------------ fused combine + W_UV
+
+@pytest.mark.parametrize("q_len,causal", [(1, False), (2, True)])
+def test_combine_out_proj_matches_two_calls(q_len, causal):
+    cfg = scaled(BF16_RAGGED, batch=5, heads=64, paged=True, q_len=q_len, causal=causal,
+                 query_in_cache=causal)
+    inp = MLAInputs(cfg)
+    dev = to_device(inp)
+    c = cfg
+    d = mla.dims(c.batch, c.q_len, c.heads, c.d_nope, c.d_rope, c.d_latent, c.d_v,
+                 DT[c.q_dtype], DT[c.kv_dtype])
+    run_gpu(inp, num_splits=9, dev=dev)  # fills nothing we keep; warms the path
+    step = mla.DecodeStep(d, num_splits=9)
+    step.run(q_nope=dev.q_nope, q_rope=dev.q_rope, positions=dev.positions, w_uk=dev.w_uk,
+             w_uv=dev.w_uv, latent=dev.latent, rope=dev.rope, kv_row_stride=dev.kv_row_stride,
+             kv_scale=dev.kv_scale, seq_lens=dev.seq_lens, block_table=dev.block_table,
+             max_blocks_per_seq=dev.max_blocks_per_seq, max_seq_len=dev.max_seq_len,
+             causal=dev.causal, softmax_scale=dev.softmax_scale, rope_base=dev.rope_base)
+    torch.cuda.synchronize()
+    o_fused, lse_fused, o_lat_fused = step.o.clone(), step.lse.clone(), step.o_lat.clone()
+    # the same partials without writing o_lat: identical results
+    o2 = torch.empty_like(step.o)
+    mla.mla_combine_out_proj(d, 9, dev.seq_lens, step.o_part, step.lse_part, dev.w_uv, o2)
+    # the two separate calls on the same partials
+    o_lat3 = torch.empty_like(step.o_lat)
+    lse3 = torch.empty_like(step.lse)
+    o3 = torch.empty_like(step.o)
+    mla.mla_combine(d, 9, dev.seq_lens, step.o_part, step.lse_part, o_lat3, lse3)
+    mla.mla_out_proj(d, o_lat3, dev.w_uv, o3)
+    torch.cuda.synchronize()
+    assert torch.equal(o2, o_fused)
+    assert row_rel_err(_np(o_lat_fused), _np(o_lat3)) < 1e-2
+    assert row_rel_err(_np(o_fused), _np(o3)) < 1e-2
+    assert float(torch.max(torch.abs(lse_fused - lse3))) < 1e-5
