@@ -66,13 +66,16 @@ __global__ __launch_bounds__(512) void combine_proj_kernel(
   const int hf = lane >> 5, n32 = lane & 31;
 
   // W_UV[h] rows 32 cq + n32, latent half kh: in flight during phases 0-1
+  // (wave 0 issues its share after the seq_lens scan, which must not wait
+  // for them)
   bf16x8 bw[16];
-  {
+  auto load_w = [&]() {
     const int vb = 32 * cq;
     const bf16x8* bp = (const bf16x8*)(w_uv + ((int64_t)h * d_v + (vb < d_v ? vb : 0) + n32) * 512);
 #pragma unroll
     for (int k = 0; k < 16; ++k) bw[k] = bp[2 * (16 * kh + k) + hf];
-  }
+  };
+  if (w != 0) load_w();
 
   // ---- phase 0a: total tiles T and the first tile / tile count of each
   // sequence the rows touch (at most 32), by wave 0
@@ -104,8 +107,22 @@ __global__ __launch_bounds__(512) void combine_proj_kernel(
     }
     if (lane == 0) tot_T = tot;
   }
+  if (w == 0) load_w();
   __syncthreads();
   const int64_t T = tot_T;
+  // unit arithmetic in 32 bits when T G fits; with G <= T no unit is empty
+  const bool small = T * (int64_t)G < ((int64_t)1 << 32);
+  const bool may_be_empty = G > T;
+  auto unit_of = [&](int64_t x) -> int64_t {
+    return small ? (int64_t)(((uint32_t)x * (uint32_t)G + (uint32_t)G - 1u) / (uint32_t)T)
+                 : unit_of_tile(x, T, G);
+  };
+  auto nonempty = [&](int64_t u) -> bool {
+    if (!may_be_empty) return true;
+    return small ? ((uint32_t)u * (uint32_t)T) / (uint32_t)G <
+                       ((uint32_t)u * (uint32_t)T + (uint32_t)T) / (uint32_t)G
+                 : unit_begin(u, T, G) < unit_begin(u + 1, T, G);
+  };
 
   // ---- phase 0b: per row, the units and all first loads (clamped in range;
   // what an empty unit holds is never used)
@@ -125,8 +142,8 @@ __global__ __launch_bounds__(512) void combine_proj_kernel(
       r = (m % Lq) * H + h;
       const int64_t pb = seq_pb[b - b_lo], tb = seq_tb[b - b_lo];
       if (tb > 0) {
-        u0[i] = unit_of_tile(pb, T, G);
-        n[i] = (int)(unit_of_tile(pb + tb - 1, T, G) - u0[i] + 1);
+        u0[i] = unit_of(pb);
+        n[i] = (int)(unit_of(pb + tb - 1) - u0[i] + 1);
       }
     }
     slot0[i] = (u0[i] + b) * R + r;
@@ -142,17 +159,17 @@ __global__ __launch_bounds__(512) void combine_proj_kernel(
     const int j = w + kCPWaves * i, m = mb0 + j;
     const int ni = n[i];
     // empty units wrote no partial (weight 0); a row may span more than 64 units
-    const bool ne = lane < ni && unit_begin(u0[i] + lane, T, G) < unit_begin(u0[i] + lane + 1, T, G);
+    const bool ne = lane < ni && nonempty(u0[i] + lane);
     const float x = ne ? lv[i] : -INFINITY;
     float mx = x;
     for (int k = lane + 64; k < ni; k += 64)
-      if (unit_begin(u0[i] + k, T, G) < unit_begin(u0[i] + k + 1, T, G))
+      if (nonempty(u0[i] + k))
         mx = fmaxf(mx, lse_part[slot0[i] + (int64_t)k * R]);
     mx = wave_max(mx);
     float z = (mx != -INFINITY && x != -INFINITY) ? expf(x - mx) : 0.f;
     if (mx != -INFINITY)
       for (int k = lane + 64; k < ni; k += 64)
-        if (unit_begin(u0[i] + k, T, G) < unit_begin(u0[i] + k + 1, T, G))
+        if (nonempty(u0[i] + k))
           z += expf(lse_part[slot0[i] + (int64_t)k * R] - mx);
     z = wave_sum(z);
     const float lse = mx == -INFINITY ? -INFINITY : mx + logf(z);
@@ -179,8 +196,7 @@ __global__ __launch_bounds__(512) void combine_proj_kernel(
         if (kk < ni) {
           if (kk < 64) {
             wk = lane_value(wt, kk);
-          } else if (lse != -INFINITY &&
-                     unit_begin(u0[i] + kk, T, G) < unit_begin(u0[i] + kk + 1, T, G)) {
+          } else if (lse != -INFINITY && nonempty(u0[i] + kk)) {
             wk = expf(lse_part[slot0[i] + (int64_t)kk * R] - lse);
           }
         }

@@ -34,17 +34,20 @@ __device__ __forceinline__ bf16x8 cat(bf16x4 a, bf16x4 b) {
 // sbase + voff (sbase wave-uniform, voff per lane) and the wave's 64 lanes fill
 // the 1 KB of LDS starting at byte address m0 in lane order.  Issued as
 // inline assembly so that waits on it are placed by hand (vmcnt), instead of
-// the compiler's blanket wait before every later LDS read.
+// the compiler's blanket wait before every later LDS read.  An SALU write of
+// m0 needs one wait state before a load with LDS = 1 reads it (the compiler
+// cannot pad inside the asm): without the s_nop the load may take the
+// previous m0 and fill the previous block's LDS.
 __device__ __forceinline__ void lds_dma16(const void* sbase, uint32_t voff, uint32_t m0) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(m0), "v"(voff),
-               "s"(sbase)
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(m0),
+               "v"(voff), "s"(sbase)
                : "memory", "m0");
 }
 
 // As lds_dma16 with 4 bytes per lane (256 bytes of LDS per wave).
 __device__ __forceinline__ void lds_dma4(const void* sbase, uint32_t voff, uint32_t m0) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2" ::"s"(m0), "v"(voff),
-               "s"(sbase)
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2" ::"s"(m0),
+               "v"(voff), "s"(sbase)
                : "memory", "m0");
 }
 __device__ __forceinline__ int64_t uniform64(int64_t v) {

@@ -46,6 +46,7 @@ using namespace mfma;
 constexpr int kAbsCols = 128;
 constexpr int kAbsPitch = 320;  // bytes per staged W row: 256 + 64 keeps tr reads conflict-free
 constexpr int kAbsMaxDn = 128;
+constexpr int kRopeAhead = 2;  // RoPE pairs per thread whose inputs load with W
 
 __global__ __launch_bounds__(256) void absorb_mfma_kernel(
     const uint16_t* __restrict__ q_nope, const uint16_t* __restrict__ q_rope,
@@ -74,6 +75,29 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(
   };
   bf16x8 qb[kAbsMaxDn / 32];
 
+  // RoPE work of this thread: pairs p = cb*256 + tid + i * rstride of the
+  // M * half pairs; angle pos * base^(-2k/d_r) in double, reduced into
+  // [-pi, pi], then sin/cos in single precision
+  const int half = d_r / 2, np = M * half;
+  const int rstride = (int)gridDim.y * 256;
+  int rp[kRopeAhead], rpos[kRopeAhead];
+  uint32_t rq[kRopeAhead];
+#pragma unroll
+  for (int j = 0; j < kRopeAhead; ++j) rp[j] = cb * 256 + tid + j * rstride;
+  const double l2b = half > 0 ? log2(rope_base) : 0.0;
+  auto rope_pair = [&](int p, int pos, uint32_t xq) {
+    const int m = p / half, k = p % half;
+    const double theta = exp2(-2.0 * k / d_r * l2b);
+    double ang = (double)pos * theta;
+    ang -= 6.283185307179586 * rint(ang * 0.15915494309189535);  // into [-pi, pi]
+    float sn, cs;
+    __sincosf((float)ang, &sn, &cs);
+    const float x0 = bf16_to_f32((uint16_t)(xq & 0xffffu)), x1 = bf16_to_f32((uint16_t)(xq >> 16));
+    const int64_t dst = ((int64_t)m * H + h) * W + d_c + 2 * k;
+    *(uint32_t*)(q_abs + dst) = (uint32_t)f32_to_bf16(x0 * cs - x1 * sn) |
+                                ((uint32_t)f32_to_bf16(x0 * sn + x1 * cs) << 16);
+  };
+
   // stage W_UK[h][:, cb*128 .. +128]: thread reads chunk tid%16 of rows
   // tid/16 + 16i; rows past d_n are zero (they meet zero-padded k of q)
   {
@@ -86,30 +110,26 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(
                       : make_uint4(0, 0, 0, 0);
     }
     load_q(16 * w, qb);
+    // inputs of this thread's first RoPE pairs
+#pragma unroll
+    for (int j = 0; j < kRopeAhead; ++j) {
+      const int pj = rp[j] < np ? rp[j] : 0;
+      const int m = half > 0 ? pj / half : 0, k = half > 0 ? pj % half : 0;
+      rpos[j] = rp[j] < np ? positions[m] : 0;
+      rq[j] = rp[j] < np ? *(const uint32_t*)(q_rope + ((int64_t)m * H + h) * d_r + 2 * k) : 0u;
+    }
 #pragma unroll
     for (int i = 0; i < kAbsMaxDn / 16; ++i)
       *(uint4*)(wsm + ((tid >> 4) + 16 * i) * kAbsPitch + (tid & 15) * 16) = st[i];
   }
 
-  // RoPE pairs of this head, spread over its column-block workgroups
-  const int half = d_r / 2;
-  if (half > 0) {
-    const int stride = (int)gridDim.y * 256;
-    for (int p = cb * 256 + tid; p < M * half; p += stride) {
-      const int m = p / half, k = p % half;
-      const double theta = pow(rope_base, -2.0 * k / d_r);
-      double ang = (double)positions[m] * theta;
-      ang -= 6.283185307179586 * rint(ang * 0.15915494309189535);  // into [-pi, pi]
-      float sn, cs;
-      __sincosf((float)ang, &sn, &cs);
-      const int64_t src = ((int64_t)m * H + h) * d_r + 2 * k;
-      const float x0 = bf16_to_f32(q_rope[src]), x1 = bf16_to_f32(q_rope[src + 1]);
-      const int64_t dst = ((int64_t)m * H + h) * W + d_c + 2 * k;
-      const uint32_t packed = (uint32_t)f32_to_bf16(x0 * cs - x1 * sn) |
-                              ((uint32_t)f32_to_bf16(x0 * sn + x1 * cs) << 16);
-      *(uint32_t*)(q_abs + dst) = packed;
-    }
-  }
+  // RoPE pairs of this head, spread over its column-block workgroups; the
+  // inputs of the first kRopeAhead pairs of this thread are already in
+  // flight (loaded above, before W reaches LDS)
+  for (int j = 0; j < kRopeAhead; ++j)
+    if (rp[j] < np) rope_pair(rp[j], rpos[j], rq[j]);
+  for (int p = rp[kRopeAhead - 1] + rstride; p < np; p += rstride)
+    rope_pair(p, positions[p / half], *(const uint32_t*)(q_rope + ((int64_t)(p / half) * H + h) * d_r + 2 * (p % half)));
   __syncthreads();
 
   for (int mb = 16 * w; mb < M; mb += 64) {
