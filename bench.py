@@ -11,6 +11,10 @@ all on one stream.
 The default workload is DeepSeek-V3 shaped: batch 64, 8192 cached tokens per
 sequence, 128 heads, latent 512 + RoPE 64, bf16, paged in 64-token blocks.
 
+The default warmup (500 steps, ~0.1 s) lets the GPU clock settle at its
+sustained level before the timed steps; with only a few warmup steps the
+timed region falls inside the clock ramp and reads up to ~25% slower.
+
 Prints one JSON line on stdout.  `value` is cache GB/s of the whole step
 (cached bytes / step time); `ms_per_step` gives the step latency.  The
 `roofline` object rates the decode kernel alone, timed with HIP events on
@@ -94,8 +98,11 @@ def cpu_baseline(inp, seconds: float):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    # the GPU clock takes ~100 ms of sustained load to reach its steady
+    # level; the default warmup covers that, so the timed steps measure the
+    # sustained rate of a decode loop rather than the ramp
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--num-splits", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -54,7 +54,8 @@ __global__ __launch_bounds__(512) void combine_proj_kernel(
     float* __restrict__ lse_out, uint16_t* __restrict__ o_lat) {
   __shared__ __attribute__((aligned(16))) char lat[kCPRows * kCPPitch];
   __shared__ __attribute__((aligned(16))) float red[4 * 64 * 16];
-  __shared__ int64_t seq_pb[kCPRows], seq_tb[kCPRows];
+  __shared__ int64_t row_u0[kCPRows], row_slot[kCPRows];
+  __shared__ int row_n[kCPRows];
   __shared__ int64_t tot_T;
 
   const int h = blockIdx.x;
@@ -65,9 +66,8 @@ __global__ __launch_bounds__(512) void combine_proj_kernel(
   const int cq = w & 3, kh = w >> 2;
   const int hf = lane >> 5, n32 = lane & 31;
 
-  // W_UV[h] rows 32 cq + n32, latent half kh: in flight during phases 0-1
-  // (wave 0 issues its share after the seq_lens scan, which must not wait
-  // for them)
+  // W_UV[h] rows 32 cq + n32, latent half kh: loaded after the partials
+  // (needed first), in flight during phases 0-1
   bf16x8 bw[16];
   auto load_w = [&]() {
     const int vb = 32 * cq;
@@ -75,12 +75,12 @@ __global__ __launch_bounds__(512) void combine_proj_kernel(
 #pragma unroll
     for (int k = 0; k < 16; ++k) bw[k] = bp[2 * (16 * kh + k) + hf];
   };
-  if (w != 0) load_w();
 
-  // ---- phase 0a: total tiles T and the first tile / tile count of each
-  // sequence the rows touch (at most 32), by wave 0
+  // ---- phase 0a, by wave 0: total tiles T, then for each of the 32 rows
+  // (lane j) its sequence's first split unit u0, unit count n and first
+  // partial slot (u0 + b) R + r
   const int b_lo = mb0 / Lq;
-  const int nb = mb0 < M ? (min(M, mb0 + kCPRows) - 1) / Lq - b_lo + 1 : 0;
+  const int nb = mb0 < M ? (min(M, mb0 + kCPRows) - 1) / Lq - b_lo + 1 : 0;  // <= 32
   if (w == 0) {
     int64_t tot = 0, before = 0;
 #pragma unroll 4
@@ -101,22 +101,30 @@ __global__ __launch_bounds__(512) void combine_proj_kernel(
       tot += __shfl_xor(tot, d, 64);
       before += __shfl_xor(before, d, 64);
     }
-    if (lane < nb) {
-      seq_pb[lane] = before + incl - mine;
-      seq_tb[lane] = mine;
+    const int64_t pb_mine = before + incl - mine;  // first tile of sequence b_lo + lane
+    // lane j: row m = mb0 + j
+    const int m = mb0 + lane;
+    const bool live = lane < kCPRows && m < M;
+    const int b = live ? m / Lq : b_lo;
+    const int64_t pb = __shfl(pb_mine, b - b_lo, 64), tb = __shfl(mine, b - b_lo, 64);
+    int64_t u0 = 0;
+    int n = 0;
+    if (live && tb > 0) {
+      u0 = unit_of_tile(pb, tot, G);
+      n = (int)(unit_of_tile(pb + tb - 1, tot, G) - u0 + 1);
+    }
+    if (lane < kCPRows) {
+      row_u0[lane] = u0;
+      row_n[lane] = n;
+      row_slot[lane] = (u0 + b) * R + (live ? (m % Lq) * H + h : h);
     }
     if (lane == 0) tot_T = tot;
   }
-  if (w == 0) load_w();
   __syncthreads();
   const int64_t T = tot_T;
-  // unit arithmetic in 32 bits when T G fits; with G <= T no unit is empty
-  const bool small = T * (int64_t)G < ((int64_t)1 << 32);
+  // with G <= T no unit is empty
   const bool may_be_empty = G > T;
-  auto unit_of = [&](int64_t x) -> int64_t {
-    return small ? (int64_t)(((uint32_t)x * (uint32_t)G + (uint32_t)G - 1u) / (uint32_t)T)
-                 : unit_of_tile(x, T, G);
-  };
+  const bool small = T * (int64_t)G < ((int64_t)1 << 32);
   auto nonempty = [&](int64_t u) -> bool {
     if (!may_be_empty) return true;
     return small ? ((uint32_t)u * (uint32_t)T) / (uint32_t)G <
@@ -124,34 +132,25 @@ __global__ __launch_bounds__(512) void combine_proj_kernel(
                  : unit_begin(u, T, G) < unit_begin(u + 1, T, G);
   };
 
-  // ---- phase 0b: per row, the units and all first loads (clamped in range;
-  // what an empty unit holds is never used)
+  // ---- phase 0b: the first loads of this wave's rows (clamped in range;
+  // what an empty unit holds is never used), then W_UV
   const int c = 8 * lane;  // latent columns of this lane in phase 1
-  int64_t u0[kCPRowsPerWave], slot0[kCPRowsPerWave];  // slot0 = (u0 + b) R + r
+  int64_t u0[kCPRowsPerWave], slot0[kCPRowsPerWave];
   int n[kCPRowsPerWave];
   float lv[kCPRowsPerWave];
   h8 v[kCPRowsPerWave][kCPChunk];
 #pragma unroll
   for (int i = 0; i < kCPRowsPerWave; ++i) {
-    const int m = mb0 + w + kCPWaves * i;
-    u0[i] = 0;
-    n[i] = 0;
-    int b = 0, r = h;
-    if (m < M) {
-      b = m / Lq;
-      r = (m % Lq) * H + h;
-      const int64_t pb = seq_pb[b - b_lo], tb = seq_tb[b - b_lo];
-      if (tb > 0) {
-        u0[i] = unit_of(pb);
-        n[i] = (int)(unit_of(pb + tb - 1) - u0[i] + 1);
-      }
-    }
-    slot0[i] = (u0[i] + b) * R + r;
+    const int j = w + kCPWaves * i;
+    u0[i] = uniform64(row_u0[j]);
+    n[i] = __builtin_amdgcn_readfirstlane(row_n[j]);
+    slot0[i] = uniform64(row_slot[j]);
     lv[i] = lse_part[slot0[i] + (int64_t)(lane < n[i] ? lane : 0) * R];
 #pragma unroll
     for (int k = 0; k < kCPChunk; ++k)
       v[i][k] = *(const h8*)(o_part + (slot0[i] + (int64_t)(k < n[i] ? k : 0) * R) * 512 + c);
   }
+  load_w();
 
   // ---- phase 0c / 1: LSE, weights, weighted sum of the partials
 #pragma unroll

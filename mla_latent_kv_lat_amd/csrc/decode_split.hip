@@ -128,9 +128,9 @@ __device__ __forceinline__ void issue_one(const DmaPlan& p, int w, int j) {
   const int cg = (w >> 2) + 2 * j;
   const uint32_t m0 = p.dst + (uint32_t)((w + 8 * j) * 1024);
   if (cg < 8)
-    lds_dma16(p.lat, p.voff + cg * 128, m0);
+    lds_dma16_stream(p.lat, p.voff + cg * 128, m0);
   else
-    lds_dma16(p.rop, p.voff, m0);
+    lds_dma16_stream(p.rop, p.voff, m0);
 }
 
 __device__ __forceinline__ void issue_all(const DmaPlan& p, int w) {
@@ -187,9 +187,9 @@ __device__ __forceinline__ void issue_all_f8(const F8Plan& p, int w) {
   for (int i = 0; i < 3; ++i) {
     const int k = w + 8 * i;
     if (k < 16)
-      lds_dma16(p.lat, p.voff[i], p.dst + (uint32_t)(k * 1024));
+      lds_dma16_stream(p.lat, p.voff[i], p.dst + (uint32_t)(k * 1024));
     else if (k < 18)
-      lds_dma16(p.rop, p.voff[i], p.dst + (uint32_t)(k * 1024));
+      lds_dma16_stream(p.rop, p.voff[i], p.dst + (uint32_t)(k * 1024));
     else if (k == 18)
       lds_dma4(p.scl, p.voff[i], p.dst + 18432u);
   }

@@ -44,6 +44,15 @@ __device__ __forceinline__ void lds_dma16(const void* sbase, uint32_t voff, uint
                : "memory", "m0");
 }
 
+// As lds_dma16 for data read once (the cache rows of a decode step): the
+// non-temporal hint keeps the stream from displacing data that later
+// kernels reuse (weights, partials) from the caches.
+__device__ __forceinline__ void lds_dma16_stream(const void* sbase, uint32_t voff, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 nt" ::"s"(m0),
+               "v"(voff), "s"(sbase)
+               : "memory", "m0");
+}
+
 // As lds_dma16 with 4 bytes per lane (256 bytes of LDS per wave).
 __device__ __forceinline__ void lds_dma4(const void* sbase, uint32_t voff, uint32_t m0) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2" ::"s"(m0),

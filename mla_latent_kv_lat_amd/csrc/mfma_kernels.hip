@@ -46,7 +46,7 @@ using namespace mfma;
 constexpr int kAbsCols = 128;
 constexpr int kAbsPitch = 320;  // bytes per staged W row: 256 + 64 keeps tr reads conflict-free
 constexpr int kAbsMaxDn = 128;
-constexpr int kRopeAhead = 2;  // RoPE pairs per thread whose inputs load with W
+constexpr int kRopeAhead = 4;  // RoPE pairs per thread whose inputs load before W
 
 __global__ __launch_bounds__(256) void absorb_mfma_kernel(
     const uint16_t* __restrict__ q_nope, const uint16_t* __restrict__ q_rope,
@@ -98,6 +98,16 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(
                                 ((uint32_t)f32_to_bf16(x0 * sn + x1 * cs) << 16);
   };
 
+  // inputs of this thread's first RoPE pairs, issued first so that their
+  // arithmetic below overlaps the W_UK and q loads
+#pragma unroll
+  for (int j = 0; j < kRopeAhead; ++j) {
+    const int pj = rp[j] < np ? rp[j] : 0;
+    const int m = half > 0 ? pj / half : 0, k = half > 0 ? pj % half : 0;
+    rpos[j] = rp[j] < np ? positions[m] : 0;
+    rq[j] = rp[j] < np ? *(const uint32_t*)(q_rope + ((int64_t)m * H + h) * d_r + 2 * k) : 0u;
+  }
+
   // stage W_UK[h][:, cb*128 .. +128]: thread reads chunk tid%16 of rows
   // tid/16 + 16i; rows past d_n are zero (they meet zero-padded k of q)
   {
@@ -110,26 +120,19 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(
                       : make_uint4(0, 0, 0, 0);
     }
     load_q(16 * w, qb);
-    // inputs of this thread's first RoPE pairs
+
+    // RoPE pairs of this head, spread over its column-block workgroups
 #pragma unroll
-    for (int j = 0; j < kRopeAhead; ++j) {
-      const int pj = rp[j] < np ? rp[j] : 0;
-      const int m = half > 0 ? pj / half : 0, k = half > 0 ? pj % half : 0;
-      rpos[j] = rp[j] < np ? positions[m] : 0;
-      rq[j] = rp[j] < np ? *(const uint32_t*)(q_rope + ((int64_t)m * H + h) * d_r + 2 * k) : 0u;
-    }
+    for (int j = 0; j < kRopeAhead; ++j)
+      if (rp[j] < np) rope_pair(rp[j], rpos[j], rq[j]);
+    for (int p = rp[kRopeAhead - 1] + rstride; p < np; p += rstride)
+      rope_pair(p, positions[p / half],
+                *(const uint32_t*)(q_rope + ((int64_t)(p / half) * H + h) * d_r + 2 * (p % half)));
+
 #pragma unroll
     for (int i = 0; i < kAbsMaxDn / 16; ++i)
       *(uint4*)(wsm + ((tid >> 4) + 16 * i) * kAbsPitch + (tid & 15) * 16) = st[i];
   }
-
-  // RoPE pairs of this head, spread over its column-block workgroups; the
-  // inputs of the first kRopeAhead pairs of this thread are already in
-  // flight (loaded above, before W reaches LDS)
-  for (int j = 0; j < kRopeAhead; ++j)
-    if (rp[j] < np) rope_pair(rp[j], rpos[j], rq[j]);
-  for (int p = rp[kRopeAhead - 1] + rstride; p < np; p += rstride)
-    rope_pair(p, positions[p / half], *(const uint32_t*)(q_rope + ((int64_t)(p / half) * H + h) * d_r + 2 * (p % half)));
   __syncthreads();
 
   for (int mb = 16 * w; mb < M; mb += 64) {
