@@ -96,11 +96,14 @@ __device__ __forceinline__ void step_sub(int64_t& x, int& hh) {
   }
 }
 
-// This wave's direct loads of half hh of tile t into LDS at `dst`: blocks
-// k = w + 8j (< 36), i.e. row group w&3, chunk groups (w>>2) + 2j; waves 0-3
-// issue 5 loads (j < 5), waves 4-7 issue 4.  Rows past the sequence end
-// re-read its last row (poisoned page tails are never touched); an empty
-// second half re-reads the first half's last row.
+// The direct loads of half hh of tile t into LDS at `dst` are issued by
+// waves 4-7 only: wave w loads row group w&3 of all 9 chunk groups (block
+// (cg, rg) = 4 cg + rg; cg 8 is the RoPE part), 9 loads.  Waves 0-3 go
+// straight on to the scores meanwhile, so the issue stall of the memory
+// pipeline overlaps matrix work, and the two waves of each SIMD leave the
+// barrier half a phase apart.  Rows past the sequence end re-read its last
+// row (poisoned page tails are never touched); an empty second half re-reads
+// the first half's last row.
 struct DmaPlan {
   const char* lat;
   const char* rop;
@@ -124,19 +127,12 @@ __device__ __forceinline__ DmaPlan plan_sub(const DecodeArgs& a, const TileInfo&
   return p;
 }
 
-__device__ __forceinline__ void issue_one(const DmaPlan& p, int w, int j) {
-  const int cg = (w >> 2) + 2 * j;
-  const uint32_t m0 = p.dst + (uint32_t)((w + 8 * j) * 1024);
-  if (cg < 8)
-    lds_dma16_stream(p.lat, p.voff + cg * 128, m0);
-  else
-    lds_dma16_stream(p.rop, p.voff, m0);
-}
-
 __device__ __forceinline__ void issue_all(const DmaPlan& p, int w) {
+  if (w < 4) return;
+  const uint32_t m0 = p.dst + (uint32_t)((w & 3) * 1024);
 #pragma unroll
-  for (int j = 0; j < 5; ++j)
-    if (j < 4 || w < 4) issue_one(p, w, j);
+  for (int cg = 0; cg < 8; ++cg) lds_dma16_stream(p.lat, p.voff + cg * 128, m0 + cg * 4096);
+  lds_dma16_stream(p.rop, p.voff, m0 + 8 * 4096);
 }
 
 // fp8 cache: staging slot = latent rows (32 x 512 B) at 0, RoPE rows
@@ -272,7 +268,7 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeArgs a) {
   const int qi = qk_active ? qrow0 / a.heads : 0;
   const int h0 = qk_active ? qrow0 % a.heads : 0;
   const int u = blockIdx.x;
-  const int my_loads = F8 ? (w < 3 ? 3 : 2) : (w < 4 ? 5 : 4);  // direct loads per sub-tile
+  const int my_loads = F8 ? (w < 3 ? 3 : 2) : (w < 4 ? 0 : 9);  // direct loads per sub-tile
 
   int64_t T, unused;
   wave_tile_sums(a.seq_lens, a.batch, 0, T, unused);
