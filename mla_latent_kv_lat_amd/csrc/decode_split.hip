@@ -96,14 +96,15 @@ __device__ __forceinline__ void step_sub(int64_t& x, int& hh) {
   }
 }
 
-// The direct loads of half hh of tile t into LDS at `dst` are issued by
-// waves 4-7 only: wave w loads row group w&3 of all 9 chunk groups (block
-// (cg, rg) = 4 cg + rg; cg 8 is the RoPE part), 9 loads.  Waves 0-3 go
-// straight on to the scores meanwhile, so the issue stall of the memory
-// pipeline overlaps matrix work, and the two waves of each SIMD leave the
-// barrier half a phase apart.  Rows past the sequence end re-read its last
-// row (poisoned page tails are never touched); an empty second half re-reads
-// the first half's last row.
+// The direct loads of half hh of tile t into LDS at `dst`: wave w loads row
+// group w&3 (block (cg, rg) = 4 cg + rg; cg 8 is the RoPE part).  Waves 4-7
+// issue chunk groups 0-4 at the top of the sub-tile, while waves 0-3 go
+// straight on to the scores; waves 0-3 issue chunk groups 5-8 after their
+// softmax, in the time they would otherwise wait at the barrier for waves
+// 4-7.  The issue stall of the memory pipeline (~130 cycles a load) thus
+// overlaps matrix work on the same SIMD instead of idling it.  Rows past the
+// sequence end re-read its last row (poisoned page tails are never
+// touched); an empty second half re-reads the first half's last row.
 struct DmaPlan {
   const char* lat;
   const char* rop;
@@ -127,12 +128,24 @@ __device__ __forceinline__ DmaPlan plan_sub(const DecodeArgs& a, const TileInfo&
   return p;
 }
 
-__device__ __forceinline__ void issue_all(const DmaPlan& p, int w) {
+__device__ __forceinline__ void issue_early(const DmaPlan& p, int w) {  // waves 4-7
   if (w < 4) return;
   const uint32_t m0 = p.dst + (uint32_t)((w & 3) * 1024);
 #pragma unroll
-  for (int cg = 0; cg < 8; ++cg) lds_dma16_stream(p.lat, p.voff + cg * 128, m0 + cg * 4096);
+  for (int cg = 0; cg < 5; ++cg) lds_dma16_stream(p.lat, p.voff + cg * 128, m0 + cg * 4096);
+}
+
+__device__ __forceinline__ void issue_late(const DmaPlan& p, int w) {  // waves 0-3
+  if (w >= 4) return;
+  const uint32_t m0 = p.dst + (uint32_t)((w & 3) * 1024);
+#pragma unroll
+  for (int cg = 5; cg < 8; ++cg) lds_dma16_stream(p.lat, p.voff + cg * 128, m0 + cg * 4096);
   lds_dma16_stream(p.rop, p.voff, m0 + 8 * 4096);
+}
+
+__device__ __forceinline__ void issue_all(const DmaPlan& p, int w) {
+  issue_early(p, w);
+  issue_late(p, w);
 }
 
 // fp8 cache: staging slot = latent rows (32 x 512 B) at 0, RoPE rows
@@ -268,7 +281,7 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeArgs a) {
   const int qi = qk_active ? qrow0 / a.heads : 0;
   const int h0 = qk_active ? qrow0 % a.heads : 0;
   const int u = blockIdx.x;
-  const int my_loads = F8 ? (w < 3 ? 3 : 2) : (w < 4 ? 0 : 9);  // direct loads per sub-tile
+  const int my_loads = F8 ? (w < 3 ? 3 : 2) : (w < 4 ? 4 : 5);  // direct loads per sub-tile
 
   int64_t T, unused;
   wave_tile_sums(a.seq_lens, a.batch, 0, T, unused);
@@ -343,11 +356,20 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeArgs a) {
       wait_vm(0);
     block_sync();  // visible to all; everyone also finished sub-tile y-1
     // the loads of sub-tile y+2, into the slot every wave finished with
+    // (bf16: waves 4-7 now, waves 0-3 after their softmax)
+    DmaPlan plan{};
+    bool pending = false;
     if (y + 2 < nsub) {
       const int s2 = slot + 2 >= kRing ? slot + 2 - kRing : slot + 2;
       if (px >= win.wx + win.wn)  // slide the window to start at the tile in use
         build_window(a, cx, x1, win.b0, win.pb0, ln, win);
-      issue(tile_info(win, px), phh, s2, ln);
+      if constexpr (F8) {
+        issue(tile_info(win, px), phh, s2, ln);
+      } else {
+        plan = plan_sub(a, tile_info(win, px), phh, lds0 + (uint32_t)(s2 * L::kStage), w, ln);
+        pending = true;
+        issue_early(plan, w);
+      }
       step_sub(px, phh);
     }
 
@@ -452,6 +474,8 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeArgs a) {
       // every wave publishes its factors (1 when unchanged): a rescale reads all rows
       if ((ln >> 4) == 0) alpha_buf[16 * w + (ln & 15)] = alpha;
       if (lane == 0) flags[w] = need ? 1 : 0;
+      if constexpr (!F8)
+        if (pending) issue_late(plan, w);
       block_sync();
 
       // ---------------- rescale (rare), then O[:, 64w..] += P V
@@ -490,6 +514,9 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeArgs a) {
           for (int nb = 0; nb < 2; ++nb) o[mb][nb] = mfma32(pa[mb], vb[nb], o[mb][nb]);
       }
     }
+
+    if constexpr (!F8)
+      if (pending && !has_tokens) issue_late(plan, w);
 
     // ---- end of this unit's part of the sequence: write the partial
     const bool last = y + 1 >= nsub || (chh == 1 && ci.rem <= kTile);
