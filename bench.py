@@ -208,8 +208,16 @@ def main():
     torch.cuda.synchronize()
     kern_ms = [float(np.mean([evs[k][j][0].elapsed_time(evs[k][j][1]) for k in range(args.steps)]))
                for j in range(len(parts))]
+    # per-step spread from the same pass (first kernel's start to last kernel's end)
+    step_us = np.array([evs[k][0][0].elapsed_time(evs[k][-1][1]) for k in range(args.steps)]) * 1e3
+    step_pct = [round(float(np.percentile(step_us, q)), 2) for q in (10, 50, 90)]
 
     acc = accounting(inp)
+    # bytes a step touches: cache, weights, activations and the split-K workspaces; below the
+    # 256 MB Infinity Cache the repeated steps are served from it and the number is labelled
+    ws_bytes = acc["step_bytes"] + step.o_part.numel() * step.o_part.element_size() + \
+        step.q_abs.numel() * step.q_abs.element_size()
+    mall_hot = ws_bytes < 256 * 2**20
     us_step = ms_step * 1e3
     cache_gbs = acc["cache_bytes"] / (ms_step * 1e-3) / 1e9
     tflops = acc["step_flops"] / (ms_step * 1e-3) / 1e12
@@ -219,15 +227,17 @@ def main():
     dec_tflops = acc["attn_flops"] / dec_s / 1e12
 
     traffic = None
+    util = None
     tpath = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
                          "decode_split_b64_l8k_paged_counters.json")
     if os.path.exists(tpath):
         try:
             with open(tpath) as f:
                 tr = json.load(f)
-            from mla_latent_kv_lat_amd.build import source_digest
-            if tr.get("source_digest") == source_digest() and tr.get("workload") == name:
+            from mla_latent_kv_lat_amd.build import DECODE_SOURCES, source_digest
+            if tr.get("source_digest") == source_digest(DECODE_SOURCES) and tr.get("workload") == name:
                 traffic = tr.get("hbm_bytes_per_launch")
+                util = tr.get("utilisation")
         except Exception as e:  # a stale or unreadable summary just leaves traffic unknown
             log(f"[bench] traffic summary not used: {e}")
 
@@ -241,6 +251,7 @@ def main():
         "ms_per_step": round(ms_step, 5),
         "us_per_step": round(us_step, 2),
         "eager_us_per_step": round(ms_eager * 1e3, 2),
+        "step_us_p10_p50_p90": step_pct,
         "tflops": round(tflops, 2),
         "pct_roofline": round(100.0 * t_roof / (ms_step * 1e-3), 2),
         "higher_is_better": True,
@@ -253,6 +264,8 @@ def main():
                    "d_latent": cfg.d_latent, "d_rope": cfg.d_rope, "d_nope": cfg.d_nope,
                    "d_v": cfg.d_v, "paged_block": 64 if cfg.paged else 0,
                    "kv_dtype": cfg.kv_dtype, "num_splits": G, "parallelism": "single GPU",
+                   "working_set_MB": round(ws_bytes / 1e6, 1),
+                   "infinity_cache_hot": bool(mall_hot),
                    "launch": "HIP graph replay of the three kernels (eager time beside)"},
         "kernels_us": {"absorb_q": round(kern_ms[0] * 1e3, 2), "decode_attn": round(kern_ms[1] * 1e3, 2),
                        "combine_out_proj": round(kern_ms[2] * 1e3, 2)},
@@ -260,7 +273,8 @@ def main():
                      "unit": "GB/s", "frac": round(dec_gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
                      "kernel": "decode_split_kernel",
                      "mfma_tflops": round(dec_tflops, 1),
-                     "mfma_frac": round(dec_tflops / PEAK_BF16_TFLOPS, 4)},
+                     "mfma_frac": round(dec_tflops / PEAK_BF16_TFLOPS, 4),
+                     "counters": util},
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a sample ...")

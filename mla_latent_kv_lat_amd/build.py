@@ -48,12 +48,18 @@ def _compile(src: str) -> str:
     return obj
 
 
-def source_digest() -> str:
-    """Hash of the library's sources and header (ties measurements to code)."""
+# sources the split-K decode kernel is built from (its measurements are tied to these)
+DECODE_SOURCES = ("decode_split.hip", "decode_common.hpp", "mfma_common.hpp", "common.hpp",
+                  "kernels.hpp")
+
+
+def source_digest(files=None) -> str:
+    """Hash of library sources and the header (ties measurements to code):
+    all sources, or only `files` (names under csrc/)."""
     import hashlib
     h = hashlib.sha256()
-    files = sorted(f for f in os.listdir(CSRC) if f.endswith((".hip", ".hpp")))
-    for f in files:
+    names = sorted(files) if files else sorted(f for f in os.listdir(CSRC) if f.endswith((".hip", ".hpp")))
+    for f in names:
         with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(f.encode() + b"\0" + fh.read())
     with open(os.path.join(HERE, "..", "include", "mla.h"), "rb") as fh:
