@@ -90,6 +90,47 @@ __device__ void build_window(const DecodeArgs& a, int64_t wx, int64_t x1, int b_
   wait_vm0();
 }
 
+// Batches of at most 64 sequences: the unit's tile range [x0, x1) of G over
+// all T tiles and the window of its first tiles from one load of seq_lens
+// (one sequence per lane) and one of block_table, instead of separate passes
+// for T, for the sequence holding x0 and for the window.  False: the unit
+// is empty.  Ends with all vector memory drained.
+__device__ bool unit_window_small(const DecodeArgs& a, int u, int lane, int64_t& x0,
+                                  int64_t& x1, TileWin& win) {
+  const int len_l = lane < a.batch ? a.seq_lens[lane] : 0;  // sequence `lane`
+  const int64_t t_l = tiles_of(len_l);
+  int64_t e = t_l;  // end tile (exclusive) of sequence `lane`
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int64_t o = __shfl_up(e, d, 64);
+    if (lane >= d) e += o;
+  }
+  const int64_t T = readlane64(e, 63);
+  x0 = unit_begin(u, T, a.num_splits);
+  x1 = unit_begin(u + 1, T, a.num_splits);
+  if (x0 >= x1) return false;
+  // lane i describes tile x = x0 + i: its sequence is the number of
+  // sequences that end at or before x (empty ones included)
+  const int64_t x = x0 + lane;
+  int cnt = 0;
+  for (int j = 0; j < a.batch; ++j) cnt += readlane64(e, j) <= x ? 1 : 0;
+  const bool ok = x < x1;  // then cnt < batch: tile x belongs to a real sequence
+  const int b = ok ? cnt : 0;
+  const int64_t start = __shfl(e - t_l, b, 64);  // first tile of sequence b
+  const int tis = (int)(x - start);
+  const int len = __shfl(len_l, b, 64);
+  const int page = ok && a.block_table ? a.block_table[(int64_t)b * a.mbps + tis] : 0;
+  win.wx = x0;
+  win.wn = (int)min((int64_t)64, x1 - x0);
+  win.b0 = __builtin_amdgcn_readfirstlane(b);
+  win.pb0 = uniform64(start);
+  win.b = b;
+  win.rem = ok ? len - tis * kTile : 0;
+  win.row0 = a.block_table ? page * kTile : (int)((int64_t)b * a.max_seq_len + (int64_t)tis * kTile);
+  wait_vm0();
+  return true;
+}
+
 __device__ __forceinline__ TileInfo tile_info(const TileWin& win, int64_t x) {
   const int i = (int)(x - win.wx);
   TileInfo t;

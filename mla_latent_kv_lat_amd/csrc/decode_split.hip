@@ -283,15 +283,17 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeArgs a) {
   const int u = blockIdx.x;
   const int my_loads = F8 ? (w < 3 ? 3 : 2) : (w < 4 ? 4 : 5);  // direct loads per sub-tile
 
-  int64_t T, unused;
-  wave_tile_sums(a.seq_lens, a.batch, 0, T, unused);
-  T = uniform64(T);
-  const int64_t x0 = unit_begin(u, T, a.num_splits);
-  const int64_t x1 = unit_begin(u + 1, T, a.num_splits);
-  if (x0 >= x1) return;  // uniform across the workgroup
-
+  int64_t x0, x1;  // this unit's tiles
   TileWin win;
-  {
+  if (a.batch <= 64) {
+    if (!unit_window_small(a, u, lane, x0, x1, win)) return;  // uniform across the workgroup
+  } else {
+    int64_t T, unused;
+    wave_tile_sums(a.seq_lens, a.batch, 0, T, unused);
+    T = uniform64(T);
+    x0 = unit_begin(u, T, a.num_splits);
+    x1 = unit_begin(u + 1, T, a.num_splits);
+    if (x0 >= x1) return;  // uniform across the workgroup
     int b;
     int64_t pb;
     find_sequence(a.seq_lens, a.batch, x0, b, pb);
