@@ -212,7 +212,8 @@ int mla_workspace_bytes(const mla_dims_t* dims, int32_t num_splits, int64_t* o_p
                         int64_t* lse_part_bytes);
 
 /* A good num_splits for `device`: one work unit per compute unit and row
- * group of 128 query rows.  Host-only query of device properties. */
+ * group (64 query rows when queries and cache are bf16, 128 otherwise).
+ * Host-only query of device properties. */
 int mla_num_splits_hint(const mla_dims_t* dims, int32_t device, int32_t* num_splits);
 
 /*

@@ -563,6 +563,331 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeArgs a) {
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// bf16 cache, head-split kernel with specialised waves.  A workgroup takes
+// 64 of the query rows (two workgroups per 128: the second one, 128 units
+// later in launch order, runs on the same XCD and finds the tiles its sibling
+// just read in L2).  Waves 0-3 only score: wave v holds all 18 k-slices of
+// its 16 rows' absorbed query in registers and runs the online softmax;
+// waves 4-7 only sum values (wave c: the 64 rows x latent columns
+// 128c..128c+127) and issue the direct loads.  The roles overlap in time:
+//
+//   phase k   score waves: S, P of sub-tile k      value waves: P V of k-1,
+//                                                  loads of sub-tile k+2
+//
+// with P, the rescale factors and the row totals double-buffered by sub-tile
+// parity and a ring of four sub-tiles (k+2 loading, k+1 landed, k scored,
+// k-1 summed).  Each role runs its own loop over the nsub + 1 phases with one
+// barrier per phase, so a wave only keeps its own role's state live.
+constexpr int kHsRows = 64;
+constexpr int kHsRing = 4;
+struct LdsHS {
+  static constexpr int kPBuf = kHsRows * kPPitch;       // 5120
+  static constexpr int kOffP = kHsRing * kSubBytes;     // 147456: two P buffers
+  static constexpr int kOffAlpha = kOffP + 2 * kPBuf;   // 2 x 64 floats
+  static constexpr int kOffInvL = kOffAlpha + 512;      // 2 x 64 floats: 1/l or 0
+  static constexpr int kOffLse = kOffInvL + 512;        // 2 x 64 floats
+  static constexpr int kOffFlag = kOffLse + 512;        // 2 x 4 bytes
+  static constexpr int kBytes = kOffFlag + 64;          // 159296
+};
+static_assert(LdsHS::kBytes <= 163840, "LDS budget");
+
+// All nine direct loads of row group (w & 3) of a sub-tile (value waves).
+__device__ __forceinline__ void issue_rows(const DmaPlan& p, int w) {
+  const uint32_t m0 = p.dst + (uint32_t)((w & 3) * 1024);
+#pragma unroll
+  for (int cg = 0; cg < 8; ++cg) lds_dma16_stream(p.lat, p.voff + cg * 128, m0 + cg * 4096);
+  lds_dma16_stream(p.rop, p.voff, m0 + 8 * 4096);
+}
+
+// Load cg (0-7 latent, 8 RoPE) of row group (w & 3).
+__device__ __forceinline__ void issue_cg(const DmaPlan& p, int w, int cg) {
+  const uint32_t m0 = p.dst + (uint32_t)((w & 3) * 1024) + (uint32_t)(cg * 4096);
+  if (cg < 8)
+    lds_dma16_stream(p.lat, p.voff + cg * 128, m0);
+  else
+    lds_dma16_stream(p.rop, p.voff, m0);
+}
+
+__global__ __launch_bounds__(512, 1) void decode_hs_kernel(DecodeArgs a) {
+  using L = LdsHS;
+  __shared__ __attribute__((aligned(1024))) char smem[L::kBytes];
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int R = a.q_len * a.heads;
+  const int rowb = blockIdx.y * kHsRows;  // first query row of this workgroup
+  const int u = blockIdx.x;
+
+  int64_t x0, x1;  // this unit's tiles
+  TileWin win;
+  if (a.batch <= 64) {
+    if (!unit_window_small(a, u, lane, x0, x1, win)) return;  // uniform across the workgroup
+  } else {
+    int64_t T, unused;
+    wave_tile_sums(a.seq_lens, a.batch, 0, T, unused);
+    T = uniform64(T);
+    x0 = unit_begin(u, T, a.num_splits);
+    x1 = unit_begin(u + 1, T, a.num_splits);
+    if (x0 >= x1) return;  // uniform across the workgroup
+    int b;
+    int64_t pb;
+    find_sequence(a.seq_lens, a.batch, x0, b, pb);
+    build_window(a, x0, x1, __builtin_amdgcn_readfirstlane(b), uniform64(pb), lane, win);
+  }
+
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_char*)smem;
+  float* alpha_buf = (float*)(smem + L::kOffAlpha);
+  float* invl_buf = (float*)(smem + L::kOffInvL);
+  float* lse_buf = (float*)(smem + L::kOffLse);
+  uint8_t* flags = (uint8_t*)(smem + L::kOffFlag);
+  const int64_t nsub = 2 * (x1 - x0);  // a unit has >= 1 tile = 2 sub-tiles
+  int64_t cx = x0;  // tile of this wave's current sub-tile
+  int chh = 0;      // and its half
+
+  if (w >= 4) {
+    // ======================= value waves: loads, then O[:, 128c..] += P V
+    const int c = w - 4;
+    int64_t px = x0;  // next sub-tile to load
+    int phh = 0;
+    issue_rows(plan_sub(a, tile_info(win, px), phh, lds0, w, lane), w);
+    step_sub(px, phh);
+    issue_rows(plan_sub(a, tile_info(win, px), phh, lds0 + (uint32_t)kSubBytes, w, lane), w);
+    step_sub(px, phh);
+    wait_vm(9);
+    block_sync();  // sub-tile 0 in LDS
+
+    f32x16 o[2][4];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) o[mb][nb] = f32x16{};
+
+    for (int64_t k = 0; k <= nsub; ++k) {
+      // the loads of sub-tile k+2, into the slot sub-tile k-2 used, go out
+      // between the value MFMAs so that their issue stalls overlap them
+      const bool more = k + 2 < nsub;
+      DmaPlan plan{};
+      int issued = more ? 0 : 9;
+      if (more) {
+        const int ln = fresh_lane();
+        if (px >= win.wx + win.wn)  // slide the window to start at the tile in use
+          build_window(a, cx, x1, win.b0, win.pb0, ln, win);
+        plan = plan_sub(a, tile_info(win, px), phh, lds0 + (uint32_t)(((k + 2) & 3) * kSubBytes),
+                        w, ln);
+        step_sub(px, phh);
+      }
+      if (k >= 1) {  // sub-tile j = k-1, scored in the previous phase
+        const int64_t j = k - 1;
+        const int jb = (int)(j & 1);
+        const TileInfo ci = tile_info(win, cx);
+        const char* tile = smem + (int)(j & 3) * kSubBytes;
+        const char* pb = smem + L::kOffP + jb * L::kPBuf;
+        if (32 * chh < ci.rem) {
+          const uint32_t fl = *(const uint32_t*)(flags + 4 * jb);
+          if (fl != 0) {  // rare: some row moved its reference max
+            const int lr = fresh_lane();
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb) {
+              f32x16 a16;
+#pragma unroll
+              for (int r4 = 0; r4 < 4; ++r4) {
+                const f32x4 a4 = *(const f32x4*)(alpha_buf + 64 * jb + mb * 32 + 8 * r4 + 4 * (lr >> 5));
+#pragma unroll
+                for (int i = 0; i < 4; ++i) a16[4 * r4 + i] = a4[i];
+              }
+#pragma unroll
+              for (int nb = 0; nb < 4; ++nb) o[mb][nb] *= a16;
+              __builtin_amdgcn_sched_barrier(0);
+            }
+          }
+          const int lv = fresh_lane();
+          const uint32_t o_pr = off_pr(lv);
+          const uint32_t o_pv0 = off_pv(lv, 2 * c, 0), o_pv1 = off_pv(lv, 2 * c, 1);
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            bf16x8 pa[2], vb[4];
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+              pa[mb] = *(const bf16x8*)(pb + o_pr + (uint32_t)(mb * 32 * kPPitch + ks * 32));
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb) {
+              const uint32_t cb = (uint32_t)(2048 * ks + 4096 * (nb >> 1) + 512 * (nb & 1));
+              vb[nb] = cat(lds_tr4(tile, cb + o_pv0), lds_tr4(tile, cb + o_pv1));
+            }
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb) {
+              if (more) issue_cg(plan, w, 4 * ks + nb);
+#pragma unroll
+              for (int mb = 0; mb < 2; ++mb) o[mb][nb] = mfma32(pa[mb], vb[nb], o[mb][nb]);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+          }
+          issued = more ? 8 : 9;
+        }
+        const bool last = j + 1 >= nsub || (chh == 1 && ci.rem <= kTile);
+        if (last) {  // end of this unit's part of the sequence: write the partial
+          const int64_t sl = (int64_t)u + ci.b;
+          const int lw = fresh_lane();
+          if ((lw >> 4) == 0 && rowb + 16 * c + (lw & 15) < R)
+            a.lse_part[sl * R + rowb + 16 * c + (lw & 15)] = lse_buf[64 * jb + 16 * c + (lw & 15)];
+          // fp16 partial rows of 1 KB; rows past R fall outside the resource
+          // and are dropped
+          const int rows_here = min(kHsRows, R - rowb);
+          const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(
+              (_Float16*)a.o_part + (sl * R + rowb) * 512, (uint32_t)rows_here * 1024u);
+          const uint32_t vo = (uint32_t)((4 * (lw >> 5) * 512 + 128 * c + (lw & 31)) * 2);
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb) {
+            f32x16 inv16;
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+              const f32x4 l4 = *(const f32x4*)(invl_buf + 64 * jb + mb * 32 + 8 * r4 + 4 * (lw >> 5));
+#pragma unroll
+              for (int i = 0; i < 4; ++i) inv16[4 * r4 + i] = l4[i];
+            }
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb) {
+              const f32x16 vv = o[mb][nb] * inv16;
+#pragma unroll
+              for (int r = 0; r < 16; ++r) {
+                const uint32_t so = (uint32_t)((mb * 32 + 8 * (r >> 2) + (r & 3)) * 1024);
+                buffer_store_f16(vv[r], rs, vo + 64 * nb, so);
+              }
+              o[mb][nb] = f32x16{};
+            }
+          }
+          wait_vm0();  // keeps the hand-counted load waits exact
+        }
+        step_sub(cx, chh);
+      }
+      for (int cg = issued; cg < 9; ++cg) issue_cg(plan, w, cg);  // the rest (all, without a value sum)
+      if (k + 1 < nsub) wait_vm(more ? 9 : 0);  // sub-tile k+1 landed
+      block_sync();
+    }
+  } else {
+    // ======================= score waves: S = Q K^T, online softmax, P
+    const int qrow0 = rowb + 16 * w;  // rows this wave scores
+    const bool qk_active = qrow0 < R;
+    const int qi = qk_active ? qrow0 / a.heads : 0;
+    const int h0 = qk_active ? qrow0 % a.heads : 0;
+    const float sl2 = a.softmax_scale * kLog2e;
+    bf16x8 q[18];
+    float m_run = -INFINITY, l_run = 0.f;
+    bool new_seg = true;
+    block_sync();  // pairs with the value waves' first barrier
+
+    for (int64_t k = 0; k <= nsub; ++k) {
+      if (k < nsub) {
+        int ln = fresh_lane();
+        if (cx >= win.wx + win.wn) build_window(a, cx, x1, win.b0, win.pb0, ln, win);
+        const TileInfo ci = tile_info(win, cx);
+        if (new_seg) {
+          new_seg = false;
+          // unconditional (inactive waves read row 0) so q is dead between segments
+          const int li = ln & 15, g = ln >> 4;
+          const bf16x8* qp = (const bf16x8*)((const uint16_t*)a.q_abs +
+                                              (((int64_t)ci.b * a.q_len + qi) * a.heads + h0 + li) * 576);
+#pragma unroll
+          for (int kk = 0; kk < 18; ++kk) q[kk] = qp[4 * kk + g];
+          m_run = -INFINITY;
+          l_run = 0.f;
+        }
+        const int kb = (int)(k & 1);
+        const char* tile = smem + (int)(k & 3) * kSubBytes;
+        const bool has_tokens = 32 * chh < ci.rem;  // uniform: an empty second half does nothing
+        int nv = ci.rem - 32 * chh - (a.causal ? a.q_len - 1 - qi : 0);
+        nv = nv < 0 ? 0 : (nv > kSub ? kSub : nv);
+        const bool scores = has_tokens && qk_active && nv > 0;  // uniform per wave
+        const bool last = k + 1 >= nsub || (chh == 1 && ci.rem <= kTile);
+        if (has_tokens) {
+          bf16x8 pw = bf16x8{};
+          bool need = false;
+          float alpha = 1.f;
+          if (scores) {
+            // token block j x k-slice parity: four accumulator chains
+            f32x4 s[2][2] = {{f32x4{}, f32x4{}}, {f32x4{}, f32x4{}}};
+            constexpr int kPf = 4;
+            const uint32_t o_qk = off_qk(fresh_lane());
+            bf16x8 ka[kPf + 1][2];
+            auto kload = [&](int kk) {
+              const int e = kk % (kPf + 1);
+#pragma unroll
+              for (int jt = 0; jt < 2; ++jt)
+                ka[e][jt] = *(const bf16x8*)(tile + (uint32_t)((kk >> 1) * 4096 + 2048 * jt + 512 * (kk & 1)) + o_qk);
+            };
+#pragma unroll
+            for (int kk = 0; kk < kPf; ++kk) kload(kk);
+#pragma unroll
+            for (int kk = 0; kk < 18; ++kk) {
+              if (kk + kPf < 18) kload(kk + kPf);
+              const int e = kk % (kPf + 1);
+              s[0][kk & 1] = mfma16(ka[e][0], q[kk], s[0][kk & 1]);
+              s[1][kk & 1] = mfma16(ka[e][1], q[kk], s[1][kk & 1]);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+            asm volatile("s_nop 15\n\ts_nop 7" : "+v"(s[0][0]), "+v"(s[0][1]), "+v"(s[1][0]), "+v"(s[1][1]));
+            s[0][0] += s[0][1];
+            s[1][0] += s[1][1];
+            ln = fresh_lane();
+            if (nv < kSub) {  // mask the tokens past the visible end
+#pragma unroll
+              for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                  if (16 * jt + 4 * (ln >> 4) + r >= nv) s[jt][0][r] = -INFINITY;
+            }
+            // this lane's max over its 8 scores, in log2 units; the reference
+            // max moves only when a score passes it by more than 2^8
+            const float lm = fmaxf(fmaxf(fmaxf(s[0][0][0], s[0][0][1]), fmaxf(s[0][0][2], s[0][0][3])),
+                                   fmaxf(fmaxf(s[1][0][0], s[1][0][1]), fmaxf(s[1][0][2], s[1][0][3]))) * sl2;
+            need = __ballot(lm > m_run + 8.f) != 0;
+            if (need) {
+              float mt = fmaxf(lm, __shfl_xor(lm, 16, 64));
+              mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+              const float m_new = fmaxf(m_run, mt);
+              alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+              m_run = m_new;
+              l_run *= alpha;
+            }
+            const float m_use = m_run == -INFINITY ? 0.f : m_run;
+#pragma unroll
+            for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const float e = __builtin_amdgcn_exp2f(fmaf(s[jt][0][r], sl2, -m_use));
+                l_run += e;
+                pw[4 * jt + r] = (__bf16)e;
+              }
+          }
+          // P rows of this wave (zeros when it has nothing to score)
+          char* pb = smem + L::kOffP + kb * L::kPBuf;
+          const uint32_t o_pw = off_pw(fresh_lane(), w);
+          *(bf16x4*)(pb + o_pw) = __builtin_shufflevector(pw, pw, 0, 1, 2, 3);
+          *(bf16x4*)(pb + o_pw + 32) = __builtin_shufflevector(pw, pw, 4, 5, 6, 7);
+          ln = fresh_lane();
+          if ((ln >> 4) == 0) alpha_buf[64 * kb + 16 * w + (ln & 15)] = alpha;
+          if (ln == 0) flags[4 * kb + w] = need ? 1 : 0;
+        }
+        if (last) {  // the segment's row totals, for the value waves
+          float l_tot = l_run + __shfl_xor(l_run, 16, 64);
+          l_tot += __shfl_xor(l_tot, 32, 64);
+          ln = fresh_lane();
+          if ((ln >> 4) == 0) {
+            invl_buf[64 * kb + 16 * w + (ln & 15)] = l_tot > 0.f ? 1.f / l_tot : 0.f;
+            lse_buf[64 * kb + 16 * w + (ln & 15)] =
+                l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+          }
+          new_seg = true;
+        }
+        step_sub(cx, chh);
+      }
+      block_sync();
+    }
+  }
+}
+
 }  // namespace
 
 bool mfma_decode_supports(const mla_dims_t& d, int64_t row_stride, const void* latent,
@@ -575,11 +900,13 @@ bool mfma_decode_supports(const mla_dims_t& d, int64_t row_stride, const void* l
 
 hipError_t launch_decode_mfma(const mla_dims_t& d, const DecodeArgs& a, hipStream_t s) {
   const int R = d.q_len * d.heads;
-  dim3 grid((unsigned)a.num_splits, (unsigned)((R + 127) / 128));
-  if (d.kv_dtype == MLA_FP8_E4M3)
+  if (d.kv_dtype == MLA_FP8_E4M3) {
+    dim3 grid((unsigned)a.num_splits, (unsigned)((R + 127) / 128));
     hipLaunchKernelGGL(decode_split_kernel<true>, grid, dim3(512), 0, s, a);
-  else
-    hipLaunchKernelGGL(decode_split_kernel<false>, grid, dim3(512), 0, s, a);
+  } else {
+    dim3 grid((unsigned)a.num_splits, (unsigned)((R + kHsRows - 1) / kHsRows));
+    hipLaunchKernelGGL(decode_hs_kernel, grid, dim3(512), 0, s, a);
+  }
   return hipGetLastError();
 }
 
