@@ -228,14 +228,16 @@ def main():
 
     traffic = None
     util = None
+    dec_kernel = "decode_fp8_kernel" if cfg.kv_dtype == "fp8" else "decode_hs_kernel"
     tpath = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
-                         "decode_split_b64_l8k_paged_counters.json")
+                         "decode_hs_b64_l8k_paged_counters.json")
     if os.path.exists(tpath):
         try:
             with open(tpath) as f:
                 tr = json.load(f)
             from mla_latent_kv_lat_amd.build import DECODE_SOURCES, source_digest
-            if tr.get("source_digest") == source_digest(DECODE_SOURCES) and tr.get("workload") == name:
+            if (tr.get("source_digest") == source_digest(DECODE_SOURCES) and tr.get("workload") == name
+                    and tr.get("kernel") == dec_kernel):
                 traffic = tr.get("hbm_bytes_per_launch")
                 util = tr.get("utilisation")
         except Exception as e:  # a stale or unreadable summary just leaves traffic unknown
@@ -271,7 +273,7 @@ def main():
                        "combine_out_proj": round(kern_ms[2] * 1e3, 2)},
         "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(dec_gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
-                     "kernel": "decode_split_kernel",
+                     "kernel": dec_kernel,
                      "mfma_tflops": round(dec_tflops, 1),
                      "mfma_frac": round(dec_tflops / PEAK_BF16_TFLOPS, 4),
                      "counters": util},

@@ -1,27 +1,31 @@
-// Split-K MLA decode for gfx950, bf16 cache, latent 512 + RoPE 64: the
-// scores and the value sum split the workgroup's waves differently.
+// Split-K MLA decode for gfx950, latent 512 + RoPE 64, two kernels.
 //
 // Pages cited (title, section):
 //   [ARCH] "Model Architecture Driving Inference Systems: From MHA/GQA to
 //          DeepSeek MLA Matrix Absorption and Memory Minimalism"
 //
-// One workgroup = one split-K unit x 128 query rows ((query i, head h) pairs,
-// row i*H + h), 8 waves.  Per 32-token sub-tile of the cache, staged once in
-// LDS for all 128 heads ([ARCH] 3.1: every head scores the same raw latent):
+// Query rows are (query i, head h) pairs, row i*H + h.  The cache is walked
+// in 32-token sub-tiles, each staged once in LDS for all the workgroup's rows
+// ([ARCH] 3.1: every head scores the same raw latent).
 //
-//   scores   wave w owns rows 16w..16w+15: S^T = K Q^T with
+// decode_hs_kernel (bf16 cache): one workgroup = one split-K unit x 64 rows,
+// 8 waves with fixed roles, the two roles working on consecutive sub-tiles:
+//
+//   scores   waves 0-3, wave v owns rows 16v..16v+15: S^T = K Q^T with
 //            v_mfma_f32_16x16x32_bf16 (K = tile rows from LDS as A, the
-//            wave's absorbed queries as B: 13 of the 18 k-slices in
-//            registers, the last 5 in LDS); online softmax in log2 units
-//            with a lazy rescale; P (bf16) goes to a small LDS buffer.
-//   values   wave w owns latent columns 64w..64w+63 for all 128 rows:
-//            O[:, cols] += P V[:, cols] with v_mfma_f32_32x32x16_bf16
+//            wave's 18 k-slices of absorbed query in registers as B);
+//            online softmax in log2 units with a lazy rescale; P (bf16) to
+//            one of two LDS buffers.
+//   values   waves 4-7, wave c owns latent columns 128c..128c+127 of all 64
+//            rows: O[:, cols] += P V[:, cols] with v_mfma_f32_32x32x16_bf16
 //            (P from LDS as A, V = the tile's latent part read transposed
-//            with ds_read_b64_tr_b16 as B).
+//            with ds_read_b64_tr_b16 as B); they also issue the direct loads.
 //
-// Reading only its own 64 columns of V (instead of all 512) is what this
-// split buys: the LDS read instructions per tile drop by ~40% against each
-// wave doing both products for its own heads.
+// decode_fp8_kernel (fp8 e4m3 cache with per-token scales): one workgroup =
+// one split-K unit x 128 rows, every wave in both roles in turn (wave w
+// scores rows 16w.. with 11 k-slices in registers and 7 in LDS, then sums
+// latent columns 64w.. for all 128 rows); each staged sub-tile is first
+// converted exactly to bf16 in LDS, and the scales enter the scores and P.
 //
 // Operand layouts:
 //   16x16x32  A: lane l row l%16, k 8(l/16)..+7; B: column l%16, same k;
@@ -37,8 +41,8 @@
 // 8 rows x 8 chunks, block (cg, rg) at (cg*4 + rg) KB; inside, row rho /
 // chunk kappa at entry 8*(kappa ^ (rg&1)) + (rho ^ 4*((kappa ^ kappa>>1)&1)),
 // which keeps the score reads and the transposed value reads free of bank
-// conflicts.  Each block is one wave-wide direct global->LDS load.  A ring of
-// 3 sub-tiles keeps two loads in flight ahead of the one being used.
+// conflicts.  Each block is one wave-wide direct global->LDS load.  Rings of
+// 4 (bf16) and 3 (fp8 staging) sub-tiles keep two loads in flight.
 //
 // The loop is latency-bound before it is bandwidth-bound, so it avoids
 // anything that stalls a wave on memory: the unit's tile descriptors
@@ -68,22 +72,21 @@ constexpr int kPPitch = 80;                    // bytes per row of P (32 bf16 + 
 constexpr int kPBytes = 128 * kPPitch;         // 10240
 constexpr int kF8Stage = 32 * 512 + 32 * 64 + 256;  // 18688: fp8 rows + scales
 
-// LDS map.  bf16 cache: the ring of three sub-tiles is the tile itself.
-// fp8 cache: the ring stages raw e4m3 rows and per-token scales, and one
-// bf16 tile receives the exact conversion of the sub-tile in use.
-template <bool F8>
-struct Lds {
+// LDS map of the fp8 kernel: the ring stages raw e4m3 rows and per-token
+// scales, and one bf16 tile receives the exact conversion of the sub-tile in
+// use.
+struct LdsF8 {
   // k-slices of Q (32 columns each) kept in registers; the rest live in LDS
-  static constexpr int kQReg = F8 ? 11 : 13;
+  static constexpr int kQReg = 11;
   static constexpr int kQLds = 18 - kQReg;
-  static constexpr int kStage = F8 ? kF8Stage : kSubBytes;  // bytes per ring slot
-  static constexpr int kConv = kRing * kStage;               // fp8: converted tile
-  static constexpr int kOffP = F8 ? kConv + kSubBytes : kRing * kSubBytes;
+  static constexpr int kStage = kF8Stage;             // bytes per ring slot
+  static constexpr int kConv = kRing * kStage;        // the converted tile
+  static constexpr int kOffP = kConv + kSubBytes;
   static constexpr int kOffAlpha = kOffP + kPBytes;
   static constexpr int kOffL = kOffAlpha + 512;
   static constexpr int kOffFlag = kOffL + 512;
   static constexpr int kOffQ = kOffFlag + 128;
-  static constexpr int kBytes = kOffQ + kQLds * 8192;  // bf16 162944, fp8 161664
+  static constexpr int kBytes = kOffQ + kQLds * 8192;  // 161664
 };
 
 // Next 32-token sub-tile: second half of the tile, or the next tile.
@@ -96,15 +99,11 @@ __device__ __forceinline__ void step_sub(int64_t& x, int& hh) {
   }
 }
 
-// The direct loads of half hh of tile t into LDS at `dst`: wave w loads row
-// group w&3 (block (cg, rg) = 4 cg + rg; cg 8 is the RoPE part).  Waves 4-7
-// issue chunk groups 0-4 at the top of the sub-tile, while waves 0-3 go
-// straight on to the scores; waves 0-3 issue chunk groups 5-8 after their
-// softmax, in the time they would otherwise wait at the barrier for waves
-// 4-7.  The issue stall of the memory pipeline (~130 cycles a load) thus
-// overlaps matrix work on the same SIMD instead of idling it.  Rows past the
-// sequence end re-read its last row (poisoned page tails are never
-// touched); an empty second half re-reads the first half's last row.
+// The direct loads of half hh of tile t (bf16 cache) into LDS at `dst`:
+// wave w loads row group w&3, nine 1 KB blocks (block (cg, rg) = 4 cg + rg;
+// cg 8 is the RoPE part).  Rows past the sequence end re-read its last row
+// (poisoned page tails are never touched); an empty second half re-reads the
+// first half's last row.
 struct DmaPlan {
   const char* lat;
   const char* rop;
@@ -126,26 +125,6 @@ __device__ __forceinline__ DmaPlan plan_sub(const DecodeArgs& a, const TileInfo&
   p.voff = (uint32_t)(r * stride) + (uint32_t)(kappa * 16);
   p.dst = dst;
   return p;
-}
-
-__device__ __forceinline__ void issue_early(const DmaPlan& p, int w) {  // waves 4-7
-  if (w < 4) return;
-  const uint32_t m0 = p.dst + (uint32_t)((w & 3) * 1024);
-#pragma unroll
-  for (int cg = 0; cg < 5; ++cg) lds_dma16_stream(p.lat, p.voff + cg * 128, m0 + cg * 4096);
-}
-
-__device__ __forceinline__ void issue_late(const DmaPlan& p, int w) {  // waves 0-3
-  if (w >= 4) return;
-  const uint32_t m0 = p.dst + (uint32_t)((w & 3) * 1024);
-#pragma unroll
-  for (int cg = 5; cg < 8; ++cg) lds_dma16_stream(p.lat, p.voff + cg * 128, m0 + cg * 4096);
-  lds_dma16_stream(p.rop, p.voff, m0 + 8 * 4096);
-}
-
-__device__ __forceinline__ void issue_all(const DmaPlan& p, int w) {
-  issue_early(p, w);
-  issue_late(p, w);
 }
 
 // fp8 cache: staging slot = latent rows (32 x 512 B) at 0, RoPE rows
@@ -259,15 +238,13 @@ __device__ __forceinline__ uint32_t off_pr(int lane) {
 
 // Q k-slices held in LDS: rows of 64 B (row 16w + lane%16, chunk lane/16),
 // 16-byte chunk c of row r stored at chunk c ^ ((r >> 1) & 3).
-template <bool F8>
 __device__ __forceinline__ uint32_t off_ql(int lane, int w) {
   const int g = lane >> 4, li = lane & 15;
-  return (uint32_t)(Lds<F8>::kOffQ + (16 * w + li) * 64 + 16 * (g ^ ((li >> 1) & 3)));
+  return (uint32_t)(LdsF8::kOffQ + (16 * w + li) * 64 + 16 * (g ^ ((li >> 1) & 3)));
 }
 
-template <bool F8>
-__global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeArgs a) {
-  using L = Lds<F8>;
+__global__ __launch_bounds__(512, 1) void decode_fp8_kernel(DecodeArgs a) {
+  using L = LdsF8;
   __shared__ __attribute__((aligned(1024))) char smem[L::kBytes];
 
   const int lane = threadIdx.x & 63;
@@ -281,7 +258,7 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeArgs a) {
   const int qi = qk_active ? qrow0 / a.heads : 0;
   const int h0 = qk_active ? qrow0 % a.heads : 0;
   const int u = blockIdx.x;
-  const int my_loads = F8 ? (w < 3 ? 3 : 2) : (w < 4 ? 4 : 5);  // direct loads per sub-tile
+  const int my_loads = w < 3 ? 3 : 2;  // direct loads per sub-tile
 
   int64_t x0, x1;  // this unit's tiles
   TileWin win;
@@ -308,10 +285,7 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeArgs a) {
   // issue the direct loads of (tile x, half hh) into ring slot `sl`
   auto issue = [&](const TileInfo& t, int hh, int sl, int lane_) {
     const uint32_t dst = lds0 + (uint32_t)(sl * L::kStage);
-    if constexpr (F8)
-      issue_all_f8(plan_sub_f8(a, t, hh, dst, w, lane_), w);
-    else
-      issue_all(plan_sub(a, t, hh, dst, w, lane_), w);
+    issue_all_f8(plan_sub_f8(a, t, hh, dst, w, lane_), w);
   };
   const float sl2 = a.softmax_scale * kLog2e;
 
@@ -343,7 +317,7 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeArgs a) {
         for (int kk = 0; kk < kQReg; ++kk) q[kk] = qp[4 * kk + g];
 #pragma unroll
         for (int kk = kQReg; kk < 18; ++kk)
-          *(bf16x8*)(smem + off_ql<F8>(ln, w) + (kk - kQReg) * 8192) = qp[4 * kk + g];
+          *(bf16x8*)(smem + off_ql(ln, w) + (kk - kQReg) * 8192) = qp[4 * kk + g];
       }
       wait_vm0();
 #pragma unroll
@@ -358,34 +332,23 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeArgs a) {
       wait_vm(0);
     block_sync();  // visible to all; everyone also finished sub-tile y-1
     // the loads of sub-tile y+2, into the slot every wave finished with
-    // (bf16: waves 4-7 now, waves 0-3 after their softmax)
-    DmaPlan plan{};
-    bool pending = false;
     if (y + 2 < nsub) {
       const int s2 = slot + 2 >= kRing ? slot + 2 - kRing : slot + 2;
       if (px >= win.wx + win.wn)  // slide the window to start at the tile in use
         build_window(a, cx, x1, win.b0, win.pb0, ln, win);
-      if constexpr (F8) {
-        issue(tile_info(win, px), phh, s2, ln);
-      } else {
-        plan = plan_sub(a, tile_info(win, px), phh, lds0 + (uint32_t)(s2 * L::kStage), w, ln);
-        pending = true;
-        issue_early(plan, w);
-      }
+      issue(tile_info(win, px), phh, s2, ln);
       step_sub(px, phh);
     }
 
     const char* stage = smem + slot * L::kStage;
     const bool has_tokens = 32 * chh < ci.rem;  // uniform: an empty second half does nothing
-    if constexpr (F8) {
-      if (has_tokens) {  // every wave converts its share, then all may read the tile
-        int tid = (int)threadIdx.x;
-        asm volatile("" : "+v"(tid));  // recompute the addresses, do not keep them live
-        convert_f8(stage, smem + L::kConv, tid);
-        block_sync();
-      }
+    if (has_tokens) {  // every wave converts its share, then all may read the tile
+      int tid = (int)threadIdx.x;
+      asm volatile("" : "+v"(tid));  // recompute the addresses, do not keep them live
+      convert_f8(stage, smem + L::kConv, tid);
+      block_sync();
     }
-    const char* tile = F8 ? smem + L::kConv : stage;
+    const char* tile = smem + L::kConv;
     char* pb = pbuf;  // one P buffer: the barrier at the top of the next
                       // sub-tile orders its reuse after every wave's reads
     // visible tokens of this sub-tile: all up to the sequence end, or with
@@ -402,7 +365,7 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeArgs a) {
         f32x4 s[2] = {f32x4{}, f32x4{}};
         constexpr int kPf = 2;
         const int lq = fresh_lane();
-        const uint32_t o_qk = off_qk(lq), o_ql = off_ql<F8>(lq, w);
+        const uint32_t o_qk = off_qk(lq), o_ql = off_ql(lq, w);
         bf16x8 ka[kPf + 1][2], qb[kPf + 1];
         auto kload = [&](int kk) {
           const int e = kk % (kPf + 1);
@@ -424,14 +387,11 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeArgs a) {
         }
         mfma_settle(s[0]);
         mfma_settle(s[1]);
-        f32x4 sc[2];  // fp8: the tokens' dequantisation scales
-        if constexpr (F8) {
-          const float* scl = (const float*)(stage + 18432);
-          sc[0] = *(const f32x4*)(scl + 4 * (ln >> 4));
-          sc[1] = *(const f32x4*)(scl + 16 + 4 * (ln >> 4));
-          s[0] *= sc[0];
-          s[1] *= sc[1];
-        }
+        // the tokens' dequantisation scales
+        const float* scl = (const float*)(stage + 18432);
+        const f32x4 sc[2] = {*(const f32x4*)(scl + 4 * (ln >> 4)), *(const f32x4*)(scl + 16 + 4 * (ln >> 4))};
+        s[0] *= sc[0];
+        s[1] *= sc[1];
         if (nv < kSub) {  // mask the tokens past the visible end
 #pragma unroll
           for (int j = 0; j < 2; ++j)
@@ -464,7 +424,7 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeArgs a) {
             const float e = __builtin_amdgcn_exp2f(fmaf(s[j][r], sl2, -m_use));
             l_run += e;
             // fp8: the value rows in LDS are unscaled, so P carries the scale
-            pw[4 * j + r] = (__bf16)(F8 ? e * sc[j][r] : e);
+            pw[4 * j + r] = (__bf16)(e * sc[j][r]);
           }
       }
       // P rows of this wave's heads (zeros when it has nothing to score)
@@ -476,8 +436,6 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeArgs a) {
       // every wave publishes its factors (1 when unchanged): a rescale reads all rows
       if ((ln >> 4) == 0) alpha_buf[16 * w + (ln & 15)] = alpha;
       if (lane == 0) flags[w] = need ? 1 : 0;
-      if constexpr (!F8)
-        if (pending) issue_late(plan, w);
       block_sync();
 
       // ---------------- rescale (rare), then O[:, 64w..] += P V
@@ -517,8 +475,6 @@ __global__ __launch_bounds__(512, 1) void decode_split_kernel(DecodeArgs a) {
       }
     }
 
-    if constexpr (!F8)
-      if (pending && !has_tokens) issue_late(plan, w);
 
     // ---- end of this unit's part of the sequence: write the partial
     const bool last = y + 1 >= nsub || (chh == 1 && ci.rem <= kTile);
@@ -902,7 +858,7 @@ hipError_t launch_decode_mfma(const mla_dims_t& d, const DecodeArgs& a, hipStrea
   const int R = d.q_len * d.heads;
   if (d.kv_dtype == MLA_FP8_E4M3) {
     dim3 grid((unsigned)a.num_splits, (unsigned)((R + 127) / 128));
-    hipLaunchKernelGGL(decode_split_kernel<true>, grid, dim3(512), 0, s, a);
+    hipLaunchKernelGGL(decode_fp8_kernel, grid, dim3(512), 0, s, a);
   } else {
     dim3 grid((unsigned)a.num_splits, (unsigned)((R + kHsRows - 1) / kHsRows));
     hipLaunchKernelGGL(decode_hs_kernel, grid, dim3(512), 0, s, a);
