@@ -184,24 +184,31 @@ __device__ __forceinline__ void issue_all_f8(const F8Plan& p, int w) {
 }
 
 // Exact e4m3 -> bf16 conversion of a staged sub-tile into the bf16 tile
-// layout (every e4m3 value is a bf16 value).  512 threads, 2304 chunks of 8.
+// layout (every e4m3 value is a bf16 value, so the unit-scale hardware
+// conversion is exact).  512 threads, 2304 chunks of 8: thread t takes chunks
+// t + 512 i, i.e. row r0 + 7 i (+1 when the chunk index wraps) of 72 chunks.
 __device__ __forceinline__ void convert_f8(const char* stage, char* tile, int tid) {
+  int r = tid / 72, kap = tid - 72 * (tid / 72);
 #pragma unroll
   for (int i = 0; i < 5; ++i) {
-    const int c = tid + 512 * i;  // bf16 chunk: row c / 72, 16-byte chunk c % 72
-    if (i < 4 || c < 2304) {
-      const int r = c / 72, kap = c % 72;
+    if (i < 4 || tid < 2304 - 4 * 512) {
       const uint2 raw = *(const uint2*)(stage + (kap < 64 ? r * 512 + kap * 8
                                                           : 16384 + r * 64 + (kap - 64) * 8));
-      const f32x2 v0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)raw.x, false);
-      const f32x2 v1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)raw.x, true);
-      const f32x2 v2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)raw.y, false);
-      const f32x2 v3 = __builtin_amdgcn_cvt_pk_f32_fp8((int)raw.y, true);
-      const bf16x8 v = {(__bf16)v0.x, (__bf16)v0.y, (__bf16)v1.x, (__bf16)v1.y,
-                        (__bf16)v2.x, (__bf16)v2.y, (__bf16)v3.x, (__bf16)v3.y};
+      const bf16x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)raw.x, 1.0f, false);
+      const bf16x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)raw.x, 1.0f, true);
+      const bf16x2 v2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)raw.y, 1.0f, false);
+      const bf16x2 v3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)raw.y, 1.0f, true);
+      const bf16x8 v = {v0.x, v0.y, v1.x, v1.y, v2.x, v2.y, v3.x, v3.y};
       const int cg = kap >> 3, kc = kap & 7, rg = r >> 3, rho = r & 7;
       const int entry = 8 * (kc ^ (rg & 1)) + (rho ^ (4 * ((kc ^ (kc >> 1)) & 1)));
       *(bf16x8*)(tile + (cg * 4 + rg) * 1024 + entry * 16) = v;
+    }
+    // next chunk: + 512 = 7 rows + 8 chunks
+    r += 7;
+    kap += 8;
+    if (kap >= 72) {
+      kap -= 72;
+      r += 1;
     }
   }
 }
