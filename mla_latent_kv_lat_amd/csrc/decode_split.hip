@@ -731,6 +731,9 @@ __global__ __launch_bounds__(512, 1) void decode_hs_kernel(DecodeArgs a) {
     }
   } else {
     // ======================= score waves: S = Q K^T, online softmax, P
+    // Each SIMD runs one score wave and one value wave; the next phase waits
+    // on this wave's P, so its instructions go first when both are ready.
+    __builtin_amdgcn_s_setprio(3);
     const int qrow0 = rowb + 16 * w;  // rows this wave scores
     const bool qk_active = qrow0 < R;
     const int qi = qk_active ? qrow0 / a.heads : 0;
