@@ -4,8 +4,9 @@ Argument marshalling only: torch allocates the caller-owned outputs and
 split-K workspaces once; ``run`` enqueues mla_absorb_q, mla_decode_attn and
 mla_combine_out_proj (the combine and the W_UV projection in one call) on the
 current stream.  ``capture`` records the
-same three launches in a HIP graph, whose replay skips the per-launch host
-overhead (the library records kernel launches only, no memset nodes).
+same three launches (for one or more consecutive steps) in a HIP graph, whose
+replay skips the per-launch host overhead (the library records kernel
+launches only, no memset nodes).
 """
 
 from __future__ import annotations
@@ -56,9 +57,13 @@ class DecodeStep:
                                 self.o_lat if (self.keep_o_lat or not fused) else None, stream)
         return self.o
 
-    def capture(self, **kwargs) -> torch.cuda.CUDAGraph:
-        """Record one step of ``run(**kwargs)`` (without ``stream``) in a HIP
-        graph; ``replay()`` re-runs it on the same inputs and buffers."""
+    def capture(self, steps: int = 1, **kwargs) -> torch.cuda.CUDAGraph:
+        """Record ``steps`` consecutive steps of ``run(**kwargs)`` (without
+        ``stream``) in one HIP graph; ``replay()`` re-runs them on the same
+        inputs and buffers.  Several steps per graph (as a model's layers
+        would share one graph) spread the per-replay launch cost over them."""
+        if steps < 1:
+            raise ValueError("steps must be >= 1")
         cur = torch.cuda.current_stream(self.device)
         side = torch.cuda.Stream(device=self.device)
         side.wait_stream(cur)
@@ -67,5 +72,6 @@ class DecodeStep:
         cur.wait_stream(side)
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
-            self.run(**kwargs)
+            for _ in range(steps):
+                self.run(**kwargs)
         return graph

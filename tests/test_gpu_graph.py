@@ -1,6 +1,7 @@
 """A decode step recorded in a HIP graph replays to the eager result.
 
-The graph holds the kernel launches of one step.  It is replayed three
+The graph holds the kernel launches of one step, or of three consecutive
+steps on the same inputs (as the benchmark records them).  It is replayed three
 times; before each replay the outputs are cleared and an unrelated eager step
 runs on other buffers, and every replay must reproduce the eager outputs
 bit for bit (the kernels are deterministic).
@@ -31,8 +32,9 @@ def _step(inp, splits):
     return mla.DecodeStep(d, num_splits=splits), args
 
 
+@pytest.mark.parametrize("steps", [1, 3])
 @pytest.mark.parametrize("name", ["dsv3_b64_ragged_paged", "fp8_b128_l16k_q2"])
-def test_graph_replay_matches_eager(name):
+def test_graph_replay_matches_eager(name, steps):
     cfg = scaled(CONFIGS[name], batch=5, seq_len=0, len_lo=300, len_hi=3000)
     step, args = _step(MLAInputs(cfg), splits=37)
     other, other_args = _step(MLAInputs(scaled(cfg, seed=cfg.seed + 1)), splits=11)
@@ -41,7 +43,7 @@ def test_graph_replay_matches_eager(name):
     torch.cuda.synchronize()
     ref = [t.clone() for t in (step.q_abs, step.o_lat, step.lse, step.o)]
 
-    graph = step.capture(**args)
+    graph = step.capture(steps=steps, **args)
     for _ in range(3):
         other.run(**other_args)
         for t in (step.q_abs, step.o_lat, step.lse, step.o):
