@@ -9,9 +9,11 @@ from .mla_oracle import (
     bf16_to_f64,
     cache_f64,
     e4m3_to_f64,
+    kv_append,
     kv_cache_bytes_per_token,
     mla_absorbed,
     mla_decode,
+    rms_norm,
     rope_interleaved,
     stored_to_f64,
 )
@@ -20,9 +22,11 @@ __all__ = [
     "bf16_to_f64",
     "cache_f64",
     "e4m3_to_f64",
+    "kv_append",
     "kv_cache_bytes_per_token",
     "mla_absorbed",
     "mla_decode",
+    "rms_norm",
     "rope_interleaved",
     "stored_to_f64",
 ]

@@ -26,6 +26,9 @@ Readings where the pages leave a step open:
     t <= len - q_len + i (bottom-right aligned).
   * A row that sees no token gets o = 0 and lse = -inf.
   * fp8 rows are OCP E4M3 codes times one fp32 scale per token.
+  * The cache-append producer (``kv_append``): RMSNorm with eps as given by
+    the caller (the module on [MATH] uses the framework default); the new
+    token's key is rotated at its own position.
 """
 
 from __future__ import annotations
@@ -233,6 +236,38 @@ def mla_absorbed(inp, rows: Optional[Iterable] = None):
                 lse[b, i, h] = m + np.log(z)
                 o[b, i, h] = w_uv[h] @ o_lat[b, i, h]
     return {"q_lat": q_lat, "q_pe": q_pe, "o_lat": o_lat, "lse": lse, "o": o}
+
+
+# ------------------------------------------------- cache-append producer
+
+
+def rms_norm(x: np.ndarray, weight: np.ndarray, eps: float) -> np.ndarray:
+    """Root-mean-square normalisation over the last axis with a learned
+    per-channel weight ([MATH] reference module: the latent passes through
+    an RMSNorm, kv_norm, before it is cached): x / sqrt(mean(x**2) + eps) * w."""
+    x = np.asarray(x, dtype=np.float64)
+    return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps) * np.asarray(weight, np.float64)
+
+
+def kv_append(h, w_dkv, kv_norm_w, w_kr, pos, rope_base: float, eps: float):
+    """The cache row of each new token (the producer of the cached latent).
+
+    [ARCH] 2.1: the hidden state is down-projected to the latent,
+    c = W_DKV h (d_c = 512 wide); [MATH] reference module: the cached latent
+    is kv_norm(W_DKV h).  [ARCH] 2.3: the decoupled key is projected on its
+    own and rotated at the token's position, k_R = RoPE(W_KR h), shared by
+    all heads.
+
+    h: [N, d] (one row per new token); w_dkv: [d_c, d]; w_kr: [d_R, d]
+    (one row per output channel, the Linear-weight layout of the module);
+    kv_norm_w: [d_c]; pos: [N].  Returns c_kv [N, d_c] and k_rope [N, d_R]
+    in float64.
+    """
+    h = np.asarray(h, dtype=np.float64)
+    c = h @ np.asarray(w_dkv, np.float64).T
+    c_kv = rms_norm(c, kv_norm_w, eps)
+    k_rope = rope_interleaved(h @ np.asarray(w_kr, np.float64).T, np.asarray(pos), rope_base)
+    return c_kv, k_rope
 
 
 # ------------------------------------------------------- byte accounting

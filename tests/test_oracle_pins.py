@@ -337,3 +337,52 @@ def test_cache_bytes_match_pages_tables():
     assert CONFIGS["dsv3_b64_l8k_paged"].storage_bytes_per_token() == 1152
     assert CONFIGS["fp8_b128_l16k_q2"].storage_bytes_per_token() == 580
     assert CONFIGS["tiny_f32"].storage_bytes_per_token() == 192
+
+
+# --------------------------------------------------- cache-append producer
+
+
+def _append_case(n=3, d=10, dc=6, dr=4, seed=7):
+    g = np.random.default_rng(seed)
+    return (g.standard_normal((n, d)), g.standard_normal((dc, d)) / math.sqrt(d),
+            1.0 + 0.1 * g.standard_normal(dc), g.standard_normal((dr, d)) / math.sqrt(d),
+            np.array([0, 5, 130][:n]))
+
+
+def test_kv_append_brute_force():
+    """Scalar loops straight from the definitions: c = W_DKV h, RMSNorm with
+    a weight, k = RoPE(W_KR h) with pair k turned by pos * base^(-2k/d_R)."""
+    from oracle import kv_append
+
+    h, wd, gam, wr, pos = _append_case()
+    eps, base = 1e-6, 10000.0
+    ckv, kr = kv_append(h, wd, gam, wr, pos, base, eps)
+    n, d = h.shape
+    for t in range(n):
+        c = [sum(wd[j][i] * h[t][i] for i in range(d)) for j in range(wd.shape[0])]
+        ms = sum(x * x for x in c) / len(c)
+        for j in range(len(c)):
+            assert abs(ckv[t][j] - c[j] / math.sqrt(ms + eps) * gam[j]) <= 1e-12 * (1 + abs(ckv[t][j]))
+        r = [sum(wr[j][i] * h[t][i] for i in range(d)) for j in range(wr.shape[0])]
+        dr = len(r)
+        for k in range(dr // 2):
+            a = pos[t] * base ** (-2.0 * k / dr)
+            x0, x1 = r[2 * k], r[2 * k + 1]
+            assert abs(kr[t][2 * k] - (x0 * math.cos(a) - x1 * math.sin(a))) <= 1e-12
+            assert abs(kr[t][2 * k + 1] - (x0 * math.sin(a) + x1 * math.cos(a))) <= 1e-12
+
+
+def test_kv_append_norm_invariants():
+    """With a unit weight and eps = 0 the cached latent has mean square 1 per
+    token and does not change when the hidden state is scaled; the key at
+    position 0 is the plain projection."""
+    from oracle import kv_append
+
+    h, wd, _, wr, _ = _append_case(n=3, d=16, dc=8, dr=6, seed=3)
+    ones = np.ones(wd.shape[0])
+    ckv, kr = kv_append(h, wd, ones, wr, np.zeros(3), 10000.0, 0.0)
+    np.testing.assert_allclose(np.mean(ckv * ckv, axis=-1), 1.0, rtol=1e-13)
+    ckv3, kr3 = kv_append(3.0 * h, wd, ones, wr, np.zeros(3), 10000.0, 0.0)
+    np.testing.assert_allclose(ckv3, ckv, rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(kr, h @ wr.T, rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(kr3, 3.0 * kr, rtol=1e-13, atol=1e-15)
