@@ -227,6 +227,46 @@ int mla_num_splits_hint(const mla_dims_t* dims, int32_t device, int32_t* num_spl
 int mla_split_plan(int32_t batch, const int32_t* seq_lens_host, int32_t num_splits,
                    int32_t* first_unit, int32_t* last_unit, int64_t* first_tile);
 
+/*
+ * Cache-append producer: the cached row of each new token ([ARCH] 2.1 and
+ * 2.3; [MATH] reference module, the latent normalised before caching):
+ *   c_kv   = RMSNorm(W_DKV h) * kv_norm_w   (mean square over d_latent, + eps)
+ *   k_rope = RoPE(W_KR h) at positions[t]   (interleaved pairs, pair k turns
+ *                                            by pos * rope_base^(-2k/d_rope))
+ * written to latent_cache + cache_rows[t] * kv_row_stride (d_latent values)
+ * and rope_cache + cache_rows[t] * kv_row_stride (d_rope values), the row
+ * layout mla_decode_attn reads.
+ *
+ *   h          [n_tokens, d_model]   bf16 hidden states of the new tokens
+ *   w_dkv      [d_latent, d_model]   bf16 (one row per latent channel)
+ *   kv_norm_w  [d_latent]            bf16 RMSNorm weight
+ *   w_kr       [d_rope, d_model]     bf16
+ *   positions  [n_tokens]            int32 position of each new token
+ *   cache_rows [n_tokens]            int64 destination row of each token
+ *                                    (distinct rows; paging is the caller's)
+ *   workspace  mla_kv_append_workspace_bytes() bytes (fp32 partial sums)
+ * Built for d_latent 512, d_rope 64, d_model a multiple of 512, kv_dtype
+ * MLA_BF16 (kv_scale must be NULL); anything else is MLA_ERR_UNSUPPORTED.
+ * Pointers: h, weights, workspace and latent_cache 16-byte aligned,
+ * rope_cache 4-byte aligned; kv_row_stride a multiple of 8 and >= 512.
+ * Asynchronous on `stream`; the caller owns all memory.
+ */
+typedef struct mla_append_dims {
+  int32_t n_tokens;
+  int32_t d_model;
+  int32_t d_latent;
+  int32_t d_rope;
+  int32_t kv_dtype;
+} mla_append_dims_t;
+
+int mla_kv_append_workspace_bytes(const mla_append_dims_t* dims, int64_t* bytes);
+
+int mla_kv_append(const mla_append_dims_t* dims, const void* h, const void* w_dkv,
+                  const void* kv_norm_w, const void* w_kr, const int32_t* positions,
+                  float rope_base, float eps, const int64_t* cache_rows, void* latent_cache,
+                  void* rope_cache, int64_t kv_row_stride, float* kv_scale, void* workspace,
+                  void* stream);
+
 #ifdef __cplusplus
 }
 #endif

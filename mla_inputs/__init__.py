@@ -8,9 +8,10 @@ oracle and the GPU path consume what it produces.
 """
 
 from .configs import BLOCK_TOKENS, CONFIGS, HEADLINE, MLAConfig, scaled
-from .generate import MLAInputs, Pool
+from .generate import AppendInputs, MLAInputs, Pool
 
 __all__ = [
+    "AppendInputs",
     "BLOCK_TOKENS",
     "CONFIGS",
     "HEADLINE",

@@ -197,3 +197,42 @@ class MLAInputs:
                     scale[r0:r0 + n] = sc
         return Pool(rows=rows, kv_scale=scale, block_table=table,
                     max_blocks_per_seq=max_blocks, max_seq_len=c.max_seq_len)
+
+
+# Tensor ids of the cache-append producer's streams.
+_T_APP_H, _T_APP_WDKV, _T_APP_WKR, _T_APP_NORM, _T_APP_POS, _T_APP_ROWS = range(101, 107)
+
+
+@dataclass
+class AppendInputs:
+    """Seeded inputs of the cache-append producer (bf16 bit patterns).
+
+    h ~ N(0, 1) [n, d]; w_dkv ~ N(0, 1/d) [d_c, d]; w_kr ~ N(0, 1/d)
+    [d_R, d]; the RMSNorm weight ~ 1 + 0.1 N(0, 1) [d_c]; positions uniform
+    in [0, max_pos); destination rows a seeded choice of n distinct rows of
+    a pool of ``pool_rows``.
+    """
+    n: int
+    d_model: int
+    seed: int
+    d_latent: int = 512
+    d_rope: int = 64
+    max_pos: int = 131072
+    pool_rows: int = 0
+
+    def __post_init__(self):
+        n, d, dc, dr = self.n, self.d_model, self.d_latent, self.d_rope
+        f32 = np.float32
+        self.h = bf16_bits_from_f32(_rng(self.seed, _T_APP_H).standard_normal((n, d), dtype=f32))
+        self.w_dkv = bf16_bits_from_f32(
+            _rng(self.seed, _T_APP_WDKV).standard_normal((dc, d), dtype=f32) / f32(np.sqrt(d)))
+        self.w_kr = bf16_bits_from_f32(
+            _rng(self.seed, _T_APP_WKR).standard_normal((dr, d), dtype=f32) / f32(np.sqrt(d)))
+        self.kv_norm_w = bf16_bits_from_f32(
+            f32(1.0) + f32(0.1) * _rng(self.seed, _T_APP_NORM).standard_normal(dc, dtype=f32))
+        self.positions = _rng(self.seed, _T_APP_POS).integers(0, self.max_pos, n).astype(np.int32)
+        if n:
+            self.positions[0] = 0
+        pool = self.pool_rows or 2 * n + 1
+        self.pool_rows = pool
+        self.rows = _rng(self.seed, _T_APP_ROWS).permutation(pool)[:n].astype(np.int64)

@@ -41,6 +41,11 @@ class MLADims(ctypes.Structure):
         "q_dtype", "kv_dtype", "flags")]
 
 
+class MLAAppendDims(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "n_tokens", "d_model", "d_latent", "d_rope", "kv_dtype")]
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing; build it with "
@@ -58,6 +63,9 @@ def _load():
         "mla_workspace_bytes": [P, I32, ctypes.POINTER(I64), ctypes.POINTER(I64)],
         "mla_num_splits_hint": [P, I32, ctypes.POINTER(I32)],
         "mla_split_plan": [I32, VP, I32, VP, VP, VP],
+        "mla_kv_append_workspace_bytes": [ctypes.POINTER(MLAAppendDims), ctypes.POINTER(I64)],
+        "mla_kv_append": [ctypes.POINTER(MLAAppendDims), VP, VP, VP, VP, VP, F, F, VP, VP, VP,
+                          I64, VP, VP, VP],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -172,3 +180,24 @@ def mla_split_plan(seq_lens, num_splits: int):
                                fu.ctypes.data if B else None, lu.ctypes.data if B else None,
                                ft.ctypes.data if B else None), "mla_split_plan")
     return fu, lu, ft
+
+
+def append_dims(n_tokens, d_model, d_latent=512, d_rope=64, kv_dtype=BF16) -> MLAAppendDims:
+    return MLAAppendDims(n_tokens, d_model, d_latent, d_rope, kv_dtype)
+
+
+def mla_kv_append_workspace_bytes(d: MLAAppendDims) -> int:
+    out = ctypes.c_int64()
+    _check(_lib.mla_kv_append_workspace_bytes(ctypes.byref(d), ctypes.byref(out)),
+           "mla_kv_append_workspace_bytes")
+    return out.value
+
+
+def mla_kv_append(d: MLAAppendDims, h, w_dkv, kv_norm_w, w_kr, positions, rope_base, eps,
+                  cache_rows, latent_cache, rope_cache, kv_row_stride, kv_scale, workspace,
+                  stream=None):
+    _check(_lib.mla_kv_append(ctypes.byref(d), _ptr(h), _ptr(w_dkv), _ptr(kv_norm_w), _ptr(w_kr),
+                              _ptr(positions), float(rope_base), float(eps), _ptr(cache_rows),
+                              _ptr(latent_cache), _ptr(rope_cache), int(kv_row_stride),
+                              _ptr(kv_scale), _ptr(workspace), _stream(stream)),
+           "mla_kv_append")

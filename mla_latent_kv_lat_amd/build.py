@@ -20,7 +20,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmla.so")
-SOURCES = ["mla_api.hip", "generic_kernels.hip", "combine.hip", "mfma_kernels.hip", "decode_split.hip", "combine_proj.hip"]
+SOURCES = ["mla_api.hip", "generic_kernels.hip", "combine.hip", "mfma_kernels.hip", "decode_split.hip",
+           "combine_proj.hip", "kv_append.hip"]
 ARCH = "gfx950"
 
 

@@ -1,0 +1,206 @@
+// Cache-append producer for gfx950: the cached row [c_kv | k_rope] of each
+// new token, written into the latent cache at a caller-given row.
+//
+// Pages cited (title, section):
+//   [ARCH] "Model Architecture Driving Inference Systems: From MHA/GQA to
+//          DeepSeek MLA Matrix Absorption and Memory Minimalism"
+//   [MATH] "Multi-Head Latent Attention (MLA): Mathematical Foundations, ..."
+//
+//   c_kv   = RMSNorm(W_DKV h) * w_norm    ([ARCH] 2.1 down-projection; the
+//                                          [MATH] reference module normalises
+//                                          the latent before caching it)
+//   k_rope = RoPE(W_KR h, pos)             ([ARCH] 2.3 decoupled key)
+//
+// Two kernels:
+//   kv_down_kernel    the 576 output channels (512 of W_DKV, 64 of W_KR)
+//                     as one GEMM on v_mfma_f32_16x16x32_bf16, split over
+//                     the hidden width: workgroup (n-block, chunk) computes
+//                     16 channels of every token over 512 hidden columns
+//                     (4 waves x 128), the waves' sums meet in LDS, and one
+//                     fp32 partial per chunk goes to the workspace.  Both
+//                     operands have the contracted index contiguous, so
+//                     they load straight into MFMA registers; every weight
+//                     byte is read once.
+//   kv_finish_kernel  one wave per token: adds the chunks' partials,
+//                     normalises the latent (mean square over 512 channels,
+//                     fp32), applies the norm weight, rotates the key at the
+//                     token's position (angle reduced in double precision),
+//                     and stores the bf16 row.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "common.hpp"
+#include "../../include/mla.h"
+
+namespace mla {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kAppN = 576;      // output channels: latent 512 + RoPE 64
+constexpr int kAppLat = 512;
+constexpr int kAppChunk = 512;  // hidden columns per workgroup (4 waves x 128)
+
+// 16x16x32 operands: A lane l = row l%16, k 8(l/16)..+7; B lane l = column
+// l%16, same k; C lane l = column l%16, rows 4(l/16)..+3.
+__global__ __launch_bounds__(256) void kv_down_kernel(const uint16_t* __restrict__ h,
+                                                      const uint16_t* __restrict__ w_dkv,
+                                                      const uint16_t* __restrict__ w_kr,
+                                                      int n_tok, int d_model,
+                                                      float* __restrict__ part) {
+  __shared__ f32x4 red[3][4][64];
+  const int nb = blockIdx.x;  // output channels 16 nb .. 16 nb + 15
+  const int s = blockIdx.y;   // hidden columns [512 s, 512 s + 512)
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int li = lane & 15, g = lane >> 4;
+  const int n = 16 * nb + li;
+  const uint16_t* wrow = n < kAppLat ? w_dkv + (int64_t)n * d_model
+                                     : w_kr + (int64_t)(n - kAppLat) * d_model;
+  const int k0 = kAppChunk * s + 128 * w + 8 * g;
+  bf16x8 bw[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) bw[ks] = *(const bf16x8*)(wrow + k0 + 32 * ks);
+
+  for (int m0 = 0; m0 < n_tok; m0 += 64) {  // four 16-token blocks at a time
+    f32x4 acc[4];
+    bf16x8 ha[4][4];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      const int m = m0 + 16 * mb + li;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        ha[mb][ks] = m < n_tok ? *(const bf16x8*)(h + (int64_t)m * d_model + k0 + 32 * ks) : bf16x8{};
+    }
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      acc[mb] = f32x4{};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ha[mb][ks], bw[ks], acc[mb], 0, 0, 0);
+    }
+    if (w > 0)
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) red[w - 1][mb][lane] = acc[mb];
+    __syncthreads();
+    if (w == 0) {
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        const f32x4 t = acc[mb] + red[0][mb][lane] + red[1][mb][lane] + red[2][mb][lane];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int m = m0 + 16 * mb + 4 * g + r;
+          if (m < n_tok) part[((int64_t)s * n_tok + m) * kAppN + n] = t[r];
+        }
+      }
+    }
+    __syncthreads();  // red is reused by the next token group
+  }
+}
+
+__global__ __launch_bounds__(256) void kv_finish_kernel(
+    const float* __restrict__ part, int n_chunks, int n_tok, const uint16_t* __restrict__ w_norm,
+    const int32_t* __restrict__ positions, double log2_base, float eps,
+    const int64_t* __restrict__ rows, uint16_t* __restrict__ latent, uint16_t* __restrict__ rope,
+    int64_t stride) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= n_tok) return;  // uniform per wave
+  const int lane = threadIdx.x & 63;
+  f32x4 v0 = f32x4{}, v1 = f32x4{};  // latent channels 8 lane .. 8 lane + 7
+  float r0 = 0.f, r1 = 0.f;          // RoPE pair `lane` (lanes < 32)
+  for (int s = 0; s < n_chunks; ++s) {
+    const float* p = part + ((int64_t)s * n_tok + t) * kAppN;
+    v0 += *(const f32x4*)(p + 8 * lane);
+    v1 += *(const f32x4*)(p + 8 * lane + 4);
+    if (lane < 32) {
+      r0 += p[kAppLat + 2 * lane];
+      r1 += p[kAppLat + 2 * lane + 1];
+    }
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) ss += v0[i] * v0[i] + v1[i] * v1[i];
+  ss = wave_sum(ss);
+  const float inv = 1.f / sqrtf(ss * (1.f / kAppLat) + eps);
+  const uint4 wn = *(const uint4*)(w_norm + 8 * lane);
+  const uint32_t wv[4] = {wn.x, wn.y, wn.z, wn.w};
+  const float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+  uint32_t ob[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float a = v[2 * i] * inv * bf16_to_f32((uint16_t)(wv[i] & 0xffffu));
+    const float b = v[2 * i + 1] * inv * bf16_to_f32((uint16_t)(wv[i] >> 16));
+    ob[i] = (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+  }
+  const int64_t row = rows[t];
+  *(uint4*)(latent + row * stride + 8 * lane) = make_uint4(ob[0], ob[1], ob[2], ob[3]);
+  if (lane < 32) {
+    // pair k = lane turns by pos * base^(-2k/64); the angle is reduced into
+    // [-pi, pi] in double so that long positions keep their accuracy
+    const double theta = exp2(-2.0 * lane / (2 * 32) * log2_base);
+    double ang = (double)positions[t] * theta;
+    ang -= 6.283185307179586 * rint(ang * 0.15915494309189535);
+    float sn, cs;
+    __sincosf((float)ang, &sn, &cs);
+    const float x0 = r0 * cs - r1 * sn, x1 = r0 * sn + r1 * cs;
+    *(uint32_t*)(rope + row * stride + 2 * lane) =
+        (uint32_t)f32_to_bf16(x0) | ((uint32_t)f32_to_bf16(x1) << 16);
+  }
+}
+
+bool app_dims_ok(const mla_append_dims_t* d) {
+  return d && d->n_tokens >= 0 && d->d_model > 0 && d->d_latent > 0 && d->d_rope >= 0;
+}
+
+}  // namespace
+}  // namespace mla
+
+using namespace mla;
+
+extern "C" {
+
+int mla_kv_append_workspace_bytes(const mla_append_dims_t* dims, int64_t* bytes) {
+  if (!app_dims_ok(dims) || !bytes) return MLA_ERR_INVALID_ARG;
+  if (dims->d_latent != kAppLat || dims->d_rope != kAppN - kAppLat || dims->d_model % kAppChunk)
+    return MLA_ERR_UNSUPPORTED;
+  *bytes = (int64_t)(dims->d_model / kAppChunk) * dims->n_tokens * kAppN * 4;
+  return MLA_OK;
+}
+
+int mla_kv_append(const mla_append_dims_t* dims, const void* h, const void* w_dkv,
+                  const void* kv_norm_w, const void* w_kr, const int32_t* positions,
+                  float rope_base, float eps, const int64_t* cache_rows, void* latent_cache,
+                  void* rope_cache, int64_t kv_row_stride, float* kv_scale, void* workspace,
+                  void* stream) {
+  if (!app_dims_ok(dims)) return MLA_ERR_INVALID_ARG;
+  if (dims->d_latent != kAppLat || dims->d_rope != kAppN - kAppLat || dims->d_model % kAppChunk ||
+      dims->kv_dtype != MLA_BF16)
+    return MLA_ERR_UNSUPPORTED;
+  if (dims->n_tokens == 0) return MLA_OK;
+  if (!h || !w_dkv || !kv_norm_w || !w_kr || !positions || !cache_rows || !latent_cache ||
+      !rope_cache || kv_scale)
+    return MLA_ERR_INVALID_ARG;
+  if (!workspace) return MLA_ERR_WORKSPACE;
+  auto al = [](const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; };
+  if (!al(h, 16) || !al(w_dkv, 16) || !al(w_kr, 16) || !al(kv_norm_w, 16) || !al(workspace, 16) ||
+      !al(latent_cache, 16) || !al(rope_cache, 4))
+    return MLA_ERR_INVALID_ARG;
+  if (kv_row_stride < kAppLat || kv_row_stride % 8) return MLA_ERR_INVALID_ARG;
+  if (!(rope_base > 0.f) || !isfinite(rope_base) || !(eps >= 0.f) || !isfinite(eps))
+    return MLA_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  (void)hipGetLastError();
+  const int chunks = dims->d_model / kAppChunk;
+  hipLaunchKernelGGL(kv_down_kernel, dim3(kAppN / 16, chunks), dim3(256), 0, s,
+                     (const uint16_t*)h, (const uint16_t*)w_dkv, (const uint16_t*)w_kr,
+                     dims->n_tokens, dims->d_model, (float*)workspace);
+  if (hipGetLastError() != hipSuccess) return MLA_ERR_HIP;
+  hipLaunchKernelGGL(kv_finish_kernel, dim3((dims->n_tokens + 3) / 4), dim3(256), 0, s,
+                     (const float*)workspace, chunks, dims->n_tokens, (const uint16_t*)kv_norm_w,
+                     positions, log2((double)rope_base), eps, cache_rows,
+                     (uint16_t*)latent_cache, (uint16_t*)rope_cache, kv_row_stride);
+  return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+}  // extern "C"

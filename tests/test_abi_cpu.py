@@ -143,3 +143,36 @@ def test_split_plan_is_a_partition(seed):
             assert u + b not in slots
             slots.add(u + b)
     assert all(s < G + B - 1 for s in slots)
+
+
+def test_kv_append_validation():
+    """The cache-append producer's host checks (no kernel is launched)."""
+    lib = binding._lib
+    d = mla.append_dims(4, 7168)
+    ws = ctypes.c_int64()
+    assert lib.mla_kv_append_workspace_bytes(ctypes.byref(d), ctypes.byref(ws)) == 0
+    assert ws.value == 14 * 4 * 576 * 4
+    ok = dict(h=16, w_dkv=16, kv_norm_w=16, w_kr=16, positions=16, rope_base=10000.0, eps=1e-6,
+              cache_rows=16, latent_cache=16, rope_cache=16, kv_row_stride=576, kv_scale=None,
+              workspace=16)
+
+    def call(dd, **kw):
+        a = dict(ok, **kw)
+        return lib.mla_kv_append(ctypes.byref(dd), a["h"], a["w_dkv"], a["kv_norm_w"], a["w_kr"],
+                                 a["positions"], a["rope_base"], a["eps"], a["cache_rows"],
+                                 a["latent_cache"], a["rope_cache"], a["kv_row_stride"],
+                                 a["kv_scale"], a["workspace"], None)
+
+    assert call(mla.append_dims(4, 7000)) == 2          # hidden width not a multiple of 512
+    assert call(mla.append_dims(4, 7168, d_latent=256)) == 2
+    assert call(mla.append_dims(4, 7168, kv_dtype=mla.FP8_E4M3)) == 2
+    assert call(mla.append_dims(0, 7168)) == 0           # nothing to append
+    assert call(d, h=None) == 1
+    assert call(d, cache_rows=None) == 1
+    assert call(d, workspace=None) == 3
+    assert call(d, h=8) == 1                              # misaligned
+    assert call(d, kv_row_stride=100) == 1
+    assert call(d, rope_base=-1.0) == 1
+    assert call(d, eps=float("nan")) == 1
+    assert call(d, kv_scale=16) == 1
+    assert lib.mla_kv_append_workspace_bytes(None, ctypes.byref(ws)) == 1
