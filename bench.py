@@ -95,6 +95,52 @@ def cpu_baseline(inp, seconds: float):
                       f"{dt:.1f} s; value = the sample's share of the step's cache bytes / time"}
 
 
+def append_pass(mla, stream, n_tok: int, d_model: int, flush, reps: int) -> dict:
+    """Time the cache-append producer for the step's n_tok new tokens: events
+    around each launch, with a full decode step (604 MB of cache streamed at
+    the headline) between launches so that its weights come from HBM, as
+    they would between the layers of a model."""
+    import torch
+
+    from mla_inputs import AppendInputs
+
+    inp = AppendInputs(n_tok, d_model, seed=20261211)
+    dev = torch.device("cuda")
+
+    def t(a, dt):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev).view(dt)
+
+    h, wd, wr, wn = (t(a.view(np.int16), torch.bfloat16)
+                     for a in (inp.h, inp.w_dkv, inp.w_kr, inp.kv_norm_w))
+    pos = torch.from_numpy(inp.positions).to(dev)
+    rows = torch.from_numpy(inp.rows).to(dev)
+    pool = torch.empty((inp.pool_rows, 576), dtype=torch.bfloat16, device=dev)
+    d = mla.append_dims(n_tok, d_model)
+    ws = torch.empty(mla.mla_kv_append_workspace_bytes(d) // 4, dtype=torch.float32, device=dev)
+
+    def run():
+        mla.mla_kv_append(d, h, wd, wn, wr, pos, 10000.0, 1e-6, rows, pool,
+                          pool.view(-1)[512:].data_ptr(), 576, None, ws, stream)
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    run()
+    for a, b in ev:
+        flush()
+        a.record(stream)
+        run()
+        b.record(stream)
+    torch.cuda.synchronize()
+    us = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3
+    nbytes = (576 * d_model + 512) * 2 + n_tok * d_model * 2 + n_tok * (576 * 2 + 4 + 8)
+    flops = 2.0 * n_tok * 576 * d_model
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return {"us": round(us, 2), "tokens": n_tok, "d_model": d_model, "bytes": nbytes,
+            "achieved_gbs": round(gbs, 1), "peak_gbs": PEAK_HBM_GBS,
+            "frac": round(gbs / PEAK_HBM_GBS, 4), "tflops": round(flops / (us * 1e-6) / 1e12, 2),
+            "kernels": "kv_down_kernel + kv_finish_kernel"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -106,6 +152,8 @@ def main():
     ap.add_argument("--workload", default=None)
     ap.add_argument("--num-splits", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--append-d-model", type=int, default=7168,
+                    help="hidden width of the cache-append producer timed beside the step")
     ap.add_argument("--cpu-seconds", type=float, default=25.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
@@ -216,6 +264,9 @@ def main():
     step_us = np.array([evs[k][0][0].elapsed_time(evs[k][-1][1]) for k in range(args.steps)]) * 1e3
     step_pct = [round(float(np.percentile(step_us, q)), 2) for q in (10, 50, 90)]
 
+    kv_app = append_pass(mla, stream, cfg.batch * cfg.q_len, args.append_d_model,
+                         lambda: step.run(**args_run), min(args.steps, 100))
+
     acc = accounting(inp)
     # bytes a step touches: cache, weights, activations and the split-K workspaces; below the
     # 256 MB Infinity Cache the repeated steps are served from it and the number is labelled
@@ -275,6 +326,7 @@ def main():
                    "launch": f"HIP graph replay, {spg} steps of three kernels per graph (eager time beside)"},
         "kernels_us": {"absorb_q": round(kern_ms[0] * 1e3, 2), "decode_attn": round(kern_ms[1] * 1e3, 2),
                        "combine_out_proj": round(kern_ms[2] * 1e3, 2)},
+        "kv_append": kv_app,
         "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(dec_gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
                      "kernel": dec_kernel,

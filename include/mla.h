@@ -245,7 +245,7 @@ int mla_split_plan(int32_t batch, const int32_t* seq_lens_host, int32_t num_spli
  *   cache_rows [n_tokens]            int64 destination row of each token
  *                                    (distinct rows; paging is the caller's)
  *   workspace  mla_kv_append_workspace_bytes() bytes (fp32 partial sums)
- * Built for d_latent 512, d_rope 64, d_model a multiple of 512, kv_dtype
+ * Built for d_latent 512, d_rope 64, d_model a multiple of 512 up to 16384, kv_dtype
  * MLA_BF16 (kv_scale must be NULL); anything else is MLA_ERR_UNSUPPORTED.
  * Pointers: h, weights, workspace and latent_cache 16-byte aligned,
  * rope_cache 4-byte aligned; kv_row_stride a multiple of 8 and >= 512.

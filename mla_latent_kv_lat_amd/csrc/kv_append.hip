@@ -14,10 +14,10 @@
 // Two kernels:
 //   kv_down_kernel    the 576 output channels (512 of W_DKV, 64 of W_KR)
 //                     as one GEMM on v_mfma_f32_16x16x32_bf16, split over
-//                     the hidden width: workgroup (n-block, chunk) computes
-//                     16 channels of every token over 512 hidden columns
-//                     (4 waves x 128), the waves' sums meet in LDS, and one
-//                     fp32 partial per chunk goes to the workspace.  Both
+//                     the hidden width: workgroup (channel block, chunk)
+//                     computes 32 channels of every token over 512 hidden
+//                     columns (4 waves x 128), the waves' sums meet in LDS,
+//                     and one fp32 partial per chunk goes to the workspace.  Both
 //                     operands have the contracted index contiguous, so
 //                     they load straight into MFMA registers; every weight
 //                     byte is read once.
@@ -42,6 +42,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kAppN = 576;      // output channels: latent 512 + RoPE 64
 constexpr int kAppLat = 512;
 constexpr int kAppChunk = 512;  // hidden columns per workgroup (4 waves x 128)
+constexpr int kAppMaxChunks = 32;  // hidden width up to 16384 (API limit)
 
 // 16x16x32 operands: A lane l = row l%16, k 8(l/16)..+7; B lane l = column
 // l%16, same k; C lane l = column l%16, rows 4(l/16)..+3.
@@ -50,21 +51,23 @@ __global__ __launch_bounds__(256) void kv_down_kernel(const uint16_t* __restrict
                                                       const uint16_t* __restrict__ w_kr,
                                                       int n_tok, int d_model,
                                                       float* __restrict__ part) {
-  __shared__ f32x4 red[3][4][64];
-  const int nb = blockIdx.x;  // output channels 16 nb .. 16 nb + 15
-  const int s = blockIdx.y;   // hidden columns [512 s, 512 s + 512)
+  __shared__ f32x4 red[3][2][4][64];
+  const int s = blockIdx.y;  // hidden columns [512 s, 512 s + 512)
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int li = lane & 15, g = lane >> 4;
-  const int n = 16 * nb + li;
-  const uint16_t* wrow = n < kAppLat ? w_dkv + (int64_t)n * d_model
-                                     : w_kr + (int64_t)(n - kAppLat) * d_model;
   const int k0 = kAppChunk * s + 128 * w + 8 * g;
-  bf16x8 bw[4];
+  // output channels 32 blockIdx.x + 16 j + li, j = 0, 1 (never straddling 512)
+  bf16x8 bw[2][4];
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) bw[ks] = *(const bf16x8*)(wrow + k0 + 32 * ks);
+  for (int j = 0; j < 2; ++j) {
+    const int n = 32 * blockIdx.x + 16 * j + li;
+    const uint16_t* wrow = n < kAppLat ? w_dkv + (int64_t)n * d_model
+                                       : w_kr + (int64_t)(n - kAppLat) * d_model;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) bw[j][ks] = *(const bf16x8*)(wrow + k0 + 32 * ks);
+  }
 
   for (int m0 = 0; m0 < n_tok; m0 += 64) {  // four 16-token blocks at a time
-    f32x4 acc[4];
     bf16x8 ha[4][4];
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
@@ -73,25 +76,34 @@ __global__ __launch_bounds__(256) void kv_down_kernel(const uint16_t* __restrict
       for (int ks = 0; ks < 4; ++ks)
         ha[mb][ks] = m < n_tok ? *(const bf16x8*)(h + (int64_t)m * d_model + k0 + 32 * ks) : bf16x8{};
     }
+    f32x4 acc[2][4];
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-      acc[mb] = f32x4{};
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ha[mb][ks], bw[ks], acc[mb], 0, 0, 0);
-    }
+      for (int mb = 0; mb < 4; ++mb) {
+        acc[j][mb] = f32x4{};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+          acc[j][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ha[mb][ks], bw[j][ks], acc[j][mb], 0, 0, 0);
+      }
     if (w > 0)
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) red[w - 1][mb][lane] = acc[mb];
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) red[w - 1][j][mb][lane] = acc[j][mb];
     __syncthreads();
     if (w == 0) {
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
-        const f32x4 t = acc[mb] + red[0][mb][lane] + red[1][mb][lane] + red[2][mb][lane];
+      for (int j = 0; j < 2; ++j) {
+        const int n = 32 * blockIdx.x + 16 * j + li;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int m = m0 + 16 * mb + 4 * g + r;
-          if (m < n_tok) part[((int64_t)s * n_tok + m) * kAppN + n] = t[r];
+        for (int mb = 0; mb < 4; ++mb) {
+          const f32x4 t = acc[j][mb] + red[0][j][mb][lane] + red[1][j][mb][lane] + red[2][j][mb][lane];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int m = m0 + 16 * mb + 4 * g + r;
+            if (m < n_tok) part[((int64_t)s * n_tok + m) * kAppN + n] = t[r];
+          }
         }
       }
     }
@@ -109,13 +121,28 @@ __global__ __launch_bounds__(256) void kv_finish_kernel(
   const int lane = threadIdx.x & 63;
   f32x4 v0 = f32x4{}, v1 = f32x4{};  // latent channels 8 lane .. 8 lane + 7
   float r0 = 0.f, r1 = 0.f;          // RoPE pair `lane` (lanes < 32)
-  for (int s = 0; s < n_chunks; ++s) {
-    const float* p = part + ((int64_t)s * n_tok + t) * kAppN;
-    v0 += *(const f32x4*)(p + 8 * lane);
-    v1 += *(const f32x4*)(p + 8 * lane + 4);
-    if (lane < 32) {
-      r0 += p[kAppLat + 2 * lane];
-      r1 += p[kAppLat + 2 * lane + 1];
+  // eight chunks' loads in flight at once (sixteen measured slower): indices
+  // past the last chunk are clamped and the duplicates are not added, so the
+  // loads need no branches
+  constexpr int kG = 8;
+  for (int s0 = 0; s0 < n_chunks; s0 += kG) {
+    f32x4 a[kG], b[kG];
+    float2 c[kG];
+#pragma unroll
+    for (int i = 0; i < kG; ++i) {
+      const int sc = min(s0 + i, n_chunks - 1);
+      const float* p = part + ((int64_t)sc * n_tok + t) * kAppN;
+      a[i] = *(const f32x4*)(p + 8 * lane);
+      b[i] = *(const f32x4*)(p + 8 * lane + 4);
+      c[i] = *(const float2*)(p + kAppLat + 2 * (lane & 31));
+    }
+#pragma unroll
+    for (int i = 0; i < kG; ++i) {
+      const float m = s0 + i < n_chunks ? 1.f : 0.f;
+      v0 += m * a[i];
+      v1 += m * b[i];
+      r0 += m * c[i].x;
+      r1 += m * c[i].y;
     }
   }
   float ss = 0.f;
@@ -162,7 +189,8 @@ extern "C" {
 
 int mla_kv_append_workspace_bytes(const mla_append_dims_t* dims, int64_t* bytes) {
   if (!app_dims_ok(dims) || !bytes) return MLA_ERR_INVALID_ARG;
-  if (dims->d_latent != kAppLat || dims->d_rope != kAppN - kAppLat || dims->d_model % kAppChunk)
+  if (dims->d_latent != kAppLat || dims->d_rope != kAppN - kAppLat || dims->d_model % kAppChunk ||
+      dims->d_model > kAppChunk * kAppMaxChunks)
     return MLA_ERR_UNSUPPORTED;
   *bytes = (int64_t)(dims->d_model / kAppChunk) * dims->n_tokens * kAppN * 4;
   return MLA_OK;
@@ -175,7 +203,7 @@ int mla_kv_append(const mla_append_dims_t* dims, const void* h, const void* w_dk
                   void* stream) {
   if (!app_dims_ok(dims)) return MLA_ERR_INVALID_ARG;
   if (dims->d_latent != kAppLat || dims->d_rope != kAppN - kAppLat || dims->d_model % kAppChunk ||
-      dims->kv_dtype != MLA_BF16)
+      dims->d_model > kAppChunk * kAppMaxChunks || dims->kv_dtype != MLA_BF16)
     return MLA_ERR_UNSUPPORTED;
   if (dims->n_tokens == 0) return MLA_OK;
   if (!h || !w_dkv || !kv_norm_w || !w_kr || !positions || !cache_rows || !latent_cache ||
@@ -192,7 +220,7 @@ int mla_kv_append(const mla_append_dims_t* dims, const void* h, const void* w_dk
   hipStream_t s = (hipStream_t)stream;
   (void)hipGetLastError();
   const int chunks = dims->d_model / kAppChunk;
-  hipLaunchKernelGGL(kv_down_kernel, dim3(kAppN / 16, chunks), dim3(256), 0, s,
+  hipLaunchKernelGGL(kv_down_kernel, dim3(kAppN / 32, chunks), dim3(256), 0, s,
                      (const uint16_t*)h, (const uint16_t*)w_dkv, (const uint16_t*)w_kr,
                      dims->n_tokens, dims->d_model, (float*)workspace);
   if (hipGetLastError() != hipSuccess) return MLA_ERR_HIP;

@@ -164,6 +164,7 @@ def test_kv_append_validation():
                                  a["kv_scale"], a["workspace"], None)
 
     assert call(mla.append_dims(4, 7000)) == 2          # hidden width not a multiple of 512
+    assert call(mla.append_dims(4, 16896)) == 2         # wider than 16384
     assert call(mla.append_dims(4, 7168, d_latent=256)) == 2
     assert call(mla.append_dims(4, 7168, kv_dtype=mla.FP8_E4M3)) == 2
     assert call(mla.append_dims(0, 7168)) == 0           # nothing to append
