@@ -245,10 +245,15 @@ int mla_split_plan(int32_t batch, const int32_t* seq_lens_host, int32_t num_spli
  *   cache_rows [n_tokens]            int64 destination row of each token
  *                                    (distinct rows; paging is the caller's)
  *   workspace  mla_kv_append_workspace_bytes() bytes (fp32 partial sums)
- * Built for d_latent 512, d_rope 64, d_model a multiple of 512 up to 16384, kv_dtype
- * MLA_BF16 (kv_scale must be NULL); anything else is MLA_ERR_UNSUPPORTED.
- * Pointers: h, weights, workspace and latent_cache 16-byte aligned,
- * rope_cache 4-byte aligned; kv_row_stride a multiple of 8 and >= 512.
+ * kv_dtype MLA_BF16 stores bf16 values (kv_scale must be NULL);
+ * MLA_FP8_E4M3 stores OCP e4m3 codes of the row divided by its scale
+ * amax/448 (amax over the token's 576 values, fp32) and the scale to
+ * kv_scale[cache_rows[t]] (fp32), the layout mla_decode_attn reads.
+ * Built for d_latent 512, d_rope 64, d_model a multiple of 512 up to 16384;
+ * anything else is MLA_ERR_UNSUPPORTED.  Pointers: h, weights and workspace
+ * 16-byte aligned; latent_cache 16-byte (bf16) or 8-byte (fp8) aligned,
+ * rope_cache 4-byte (bf16) or 2-byte (fp8) aligned, kv_scale 4-byte
+ * aligned; kv_row_stride (elements) a multiple of 8 and >= 512.
  * Asynchronous on `stream`; the caller owns all memory.
  */
 typedef struct mla_append_dims {

@@ -25,7 +25,10 @@
 //                     normalises the latent (mean square over 512 channels,
 //                     fp32), applies the norm weight, rotates the key at the
 //                     token's position (angle reduced in double precision),
-//                     and stores the bf16 row.
+//                     and stores the bf16 row, or the e4m3 codes of the row
+//                     divided by its scale amax/448 and the scale (the fp8
+//                     cache the decode kernel reads: one fp32 scale per token
+//                     over its 576 values).
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -111,11 +114,14 @@ __global__ __launch_bounds__(256) void kv_down_kernel(const uint16_t* __restrict
   }
 }
 
+// F8: e4m3 codes (OCP) of row / scale with scale = amax / 448 over the
+// token's 576 values, and the scale to kv_scale[row]; else bf16 values.
+template <bool F8>
 __global__ __launch_bounds__(256) void kv_finish_kernel(
     const float* __restrict__ part, int n_chunks, int n_tok, const uint16_t* __restrict__ w_norm,
     const int32_t* __restrict__ positions, double log2_base, float eps,
-    const int64_t* __restrict__ rows, uint16_t* __restrict__ latent, uint16_t* __restrict__ rope,
-    int64_t stride) {
+    const int64_t* __restrict__ rows, char* __restrict__ latent, char* __restrict__ rope,
+    int64_t stride_bytes, float* __restrict__ kv_scale) {
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= n_tok) return;  // uniform per wave
   const int lane = threadIdx.x & 63;
@@ -153,26 +159,51 @@ __global__ __launch_bounds__(256) void kv_finish_kernel(
   const uint4 wn = *(const uint4*)(w_norm + 8 * lane);
   const uint32_t wv[4] = {wn.x, wn.y, wn.z, wn.w};
   const float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-  uint32_t ob[4];
+  float y[8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const float a = v[2 * i] * inv * bf16_to_f32((uint16_t)(wv[i] & 0xffffu));
-    const float b = v[2 * i + 1] * inv * bf16_to_f32((uint16_t)(wv[i] >> 16));
-    ob[i] = (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+    y[2 * i] = v[2 * i] * inv * bf16_to_f32((uint16_t)(wv[i] & 0xffffu));
+    y[2 * i + 1] = v[2 * i + 1] * inv * bf16_to_f32((uint16_t)(wv[i] >> 16));
   }
-  const int64_t row = rows[t];
-  *(uint4*)(latent + row * stride + 8 * lane) = make_uint4(ob[0], ob[1], ob[2], ob[3]);
+  // pair k = lane turns by pos * base^(-2k/64); the angle is reduced into
+  // [-pi, pi] in double so that long positions keep their accuracy
+  float x0 = 0.f, x1 = 0.f;
   if (lane < 32) {
-    // pair k = lane turns by pos * base^(-2k/64); the angle is reduced into
-    // [-pi, pi] in double so that long positions keep their accuracy
     const double theta = exp2(-2.0 * lane / (2 * 32) * log2_base);
     double ang = (double)positions[t] * theta;
     ang -= 6.283185307179586 * rint(ang * 0.15915494309189535);
     float sn, cs;
     __sincosf((float)ang, &sn, &cs);
-    const float x0 = r0 * cs - r1 * sn, x1 = r0 * sn + r1 * cs;
-    *(uint32_t*)(rope + row * stride + 2 * lane) =
-        (uint32_t)f32_to_bf16(x0) | ((uint32_t)f32_to_bf16(x1) << 16);
+    x0 = r0 * cs - r1 * sn;
+    x1 = r0 * sn + r1 * cs;
+  }
+  const int64_t row = rows[t];
+  if constexpr (F8) {
+    float am = fmaxf(fabsf(x0), fabsf(x1));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(y[i]));
+    am = wave_max(am);
+    const float sc = am > 0.f ? am / 448.f : 1.f;
+    int lo = 0, hi = 0;
+    lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[0] / sc, y[1] / sc, lo, false);
+    lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[2] / sc, y[3] / sc, lo, true);
+    hi = __builtin_amdgcn_cvt_pk_fp8_f32(y[4] / sc, y[5] / sc, hi, false);
+    hi = __builtin_amdgcn_cvt_pk_fp8_f32(y[6] / sc, y[7] / sc, hi, true);
+    *(uint2*)(latent + row * stride_bytes + 8 * lane) = make_uint2((uint32_t)lo, (uint32_t)hi);
+    if (lane < 32) {
+      const int pr = __builtin_amdgcn_cvt_pk_fp8_f32(x0 / sc, x1 / sc, 0, false);
+      *(uint16_t*)(rope + row * stride_bytes + 2 * lane) = (uint16_t)(pr & 0xffff);
+    }
+    if (lane == 0) kv_scale[row] = sc;
+  } else {
+    uint32_t ob[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      ob[i] = (uint32_t)f32_to_bf16(y[2 * i]) | ((uint32_t)f32_to_bf16(y[2 * i + 1]) << 16);
+    *(uint4*)(latent + row * stride_bytes + 16 * lane) = make_uint4(ob[0], ob[1], ob[2], ob[3]);
+    if (lane < 32)
+      *(uint32_t*)(rope + row * stride_bytes + 4 * lane) =
+          (uint32_t)f32_to_bf16(x0) | ((uint32_t)f32_to_bf16(x1) << 16);
   }
 }
 
@@ -203,16 +234,18 @@ int mla_kv_append(const mla_append_dims_t* dims, const void* h, const void* w_dk
                   void* stream) {
   if (!app_dims_ok(dims)) return MLA_ERR_INVALID_ARG;
   if (dims->d_latent != kAppLat || dims->d_rope != kAppN - kAppLat || dims->d_model % kAppChunk ||
-      dims->d_model > kAppChunk * kAppMaxChunks || dims->kv_dtype != MLA_BF16)
+      dims->d_model > kAppChunk * kAppMaxChunks ||
+      (dims->kv_dtype != MLA_BF16 && dims->kv_dtype != MLA_FP8_E4M3))
     return MLA_ERR_UNSUPPORTED;
   if (dims->n_tokens == 0) return MLA_OK;
+  const bool f8 = dims->kv_dtype == MLA_FP8_E4M3;
   if (!h || !w_dkv || !kv_norm_w || !w_kr || !positions || !cache_rows || !latent_cache ||
-      !rope_cache || kv_scale)
+      !rope_cache || (kv_scale != nullptr) != f8)
     return MLA_ERR_INVALID_ARG;
   if (!workspace) return MLA_ERR_WORKSPACE;
   auto al = [](const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; };
   if (!al(h, 16) || !al(w_dkv, 16) || !al(w_kr, 16) || !al(kv_norm_w, 16) || !al(workspace, 16) ||
-      !al(latent_cache, 16) || !al(rope_cache, 4))
+      !al(latent_cache, f8 ? 8 : 16) || !al(rope_cache, f8 ? 2 : 4) || (f8 && !al(kv_scale, 4)))
     return MLA_ERR_INVALID_ARG;
   if (kv_row_stride < kAppLat || kv_row_stride % 8) return MLA_ERR_INVALID_ARG;
   if (!(rope_base > 0.f) || !isfinite(rope_base) || !(eps >= 0.f) || !isfinite(eps))
@@ -224,10 +257,17 @@ int mla_kv_append(const mla_append_dims_t* dims, const void* h, const void* w_dk
                      (const uint16_t*)h, (const uint16_t*)w_dkv, (const uint16_t*)w_kr,
                      dims->n_tokens, dims->d_model, (float*)workspace);
   if (hipGetLastError() != hipSuccess) return MLA_ERR_HIP;
-  hipLaunchKernelGGL(kv_finish_kernel, dim3((dims->n_tokens + 3) / 4), dim3(256), 0, s,
-                     (const float*)workspace, chunks, dims->n_tokens, (const uint16_t*)kv_norm_w,
-                     positions, log2((double)rope_base), eps, cache_rows,
-                     (uint16_t*)latent_cache, (uint16_t*)rope_cache, kv_row_stride);
+  const dim3 fg((dims->n_tokens + 3) / 4);
+  if (f8)
+    hipLaunchKernelGGL(kv_finish_kernel<true>, fg, dim3(256), 0, s, (const float*)workspace,
+                       chunks, dims->n_tokens, (const uint16_t*)kv_norm_w, positions,
+                       log2((double)rope_base), eps, cache_rows, (char*)latent_cache,
+                       (char*)rope_cache, kv_row_stride, kv_scale);
+  else
+    hipLaunchKernelGGL(kv_finish_kernel<false>, fg, dim3(256), 0, s, (const float*)workspace,
+                       chunks, dims->n_tokens, (const uint16_t*)kv_norm_w, positions,
+                       log2((double)rope_base), eps, cache_rows, (char*)latent_cache,
+                       (char*)rope_cache, kv_row_stride * 2, nullptr);
   return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 

@@ -166,7 +166,8 @@ def test_kv_append_validation():
     assert call(mla.append_dims(4, 7000)) == 2          # hidden width not a multiple of 512
     assert call(mla.append_dims(4, 16896)) == 2         # wider than 16384
     assert call(mla.append_dims(4, 7168, d_latent=256)) == 2
-    assert call(mla.append_dims(4, 7168, kv_dtype=mla.FP8_E4M3)) == 2
+    assert call(mla.append_dims(4, 7168, kv_dtype=mla.FP8_E4M3)) == 1  # fp8 needs kv_scale
+    assert call(mla.append_dims(4, 7168, kv_dtype=mla.F32)) == 2
     assert call(mla.append_dims(0, 7168)) == 0           # nothing to append
     assert call(d, h=None) == 1
     assert call(d, cache_rows=None) == 1

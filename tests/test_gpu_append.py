@@ -5,6 +5,13 @@ token into its destination row of a cache pool.  Every other row of the pool
 is poisoned with NaN beforehand and must stay untouched.  Gate: 2e-2
 row-normwise (bf16), separately for the latent and the RoPE part of each row;
 the errors are bf16 rounding of the output (~2e-3).
+
+The fp8 form stores e4m3 codes of the row divided by its scale amax/448.
+The code is an integer decided in floating point, so the reference takes that
+decision as the kernel does, in fp32, from the oracle's row: the scales must
+agree to 1e-5, at most 1% of the codes may differ, each by one step (a value
+within fp32 rounding of a rounding boundary), and the dequantised row must
+match the float64 row within the fp8 gate, 5e-2 row-normwise.
 """
 
 import numpy as np
@@ -13,7 +20,8 @@ import torch
 
 import mla_latent_kv_lat_amd as mla
 from mla_inputs import AppendInputs
-from oracle import bf16_to_f64, kv_append
+from mla_inputs.generate import fp8_codes_from_f32
+from oracle import bf16_to_f64, e4m3_to_f64, kv_append
 
 pytestmark = pytest.mark.gpu
 
@@ -75,3 +83,52 @@ def test_kv_append_matches_oracle(n, d_model, stride, split_pools):
         assert (rop[inp.rows, 64:] == NAN_BITS).all()
     else:
         assert (lat[inp.rows, 576:] == NAN_BITS).all()
+
+
+@pytest.mark.parametrize("n,d_model,split_pools", [(64, 7168, False), (37, 5120, True), (3, 512, False)])
+def test_kv_append_fp8_matches_oracle(n, d_model, split_pools):
+    inp = AppendInputs(n, d_model, seed=20261220 + n)
+    dev = torch.device("cuda")
+    t = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a)).to(dev).view(dt)
+    h = t(inp.h.view(np.int16), torch.bfloat16)
+    wd = t(inp.w_dkv.view(np.int16), torch.bfloat16)
+    wr = t(inp.w_kr.view(np.int16), torch.bfloat16)
+    wn = t(inp.kv_norm_w.view(np.int16), torch.bfloat16)
+    pos = torch.from_numpy(inp.positions).to(dev)
+    rows = torch.from_numpy(inp.rows).to(dev)
+    P, stride = inp.pool_rows, 576
+    pool = torch.full((P, stride), 0x7F, dtype=torch.uint8, device=dev)   # e4m3 NaN
+    rpool = torch.full((P, stride), 0x7F, dtype=torch.uint8, device=dev) if split_pools else pool
+    scales = torch.full((P,), float("nan"), dtype=torch.float32, device=dev)
+    rope_ptr = rpool.data_ptr() if split_pools else pool.data_ptr() + 512
+    d = mla.append_dims(n, d_model, kv_dtype=mla.FP8_E4M3)
+    ws = torch.empty(mla.mla_kv_append_workspace_bytes(d) // 4, dtype=torch.float32, device=dev)
+    mla.mla_kv_append(d, h, wd, wn, wr, pos, 10000.0, 1e-6, rows, pool, rope_ptr, stride, scales, ws)
+    torch.cuda.synchronize()
+
+    ckv, kr = kv_append(bf16_to_f64(inp.h), bf16_to_f64(inp.w_dkv), bf16_to_f64(inp.kv_norm_w),
+                        bf16_to_f64(inp.w_kr), inp.positions, 10000.0, 1e-6)
+    want = np.concatenate([ckv, kr], axis=1)
+    lat = pool.cpu().numpy()
+    rop = rpool.cpu().numpy()
+    codes = np.concatenate([lat[inp.rows, :512],
+                            rop[inp.rows, :64] if split_pools else lat[inp.rows, 512:576]], axis=1)
+    sc = scales.cpu().numpy()[inp.rows]
+    # the reference decision, in fp32 as the kernel takes it
+    r32 = want.astype(np.float32)
+    am = np.abs(r32).max(axis=1)
+    sc_ref = (am / np.float32(448)).astype(np.float32)
+    ref_codes = fp8_codes_from_f32((r32 / sc_ref[:, None]).astype(np.float32))
+    assert np.all(np.abs(sc - sc_ref) <= 1e-5 * sc_ref)
+    diff = codes != ref_codes
+    assert diff.mean() <= 0.01, diff.mean()
+    c1, c2 = codes[diff].astype(int), ref_codes[diff].astype(int)
+    assert np.all((c1 >> 7) == (c2 >> 7)) and np.all(np.abs((c1 & 0x7F) - (c2 & 0x7F)) == 1)
+    got = e4m3_to_f64(codes) * sc[:, None].astype(np.float64)
+    err = np.abs(got - want).max(axis=1) / np.abs(want).max(axis=1)
+    assert err.max() < 5e-2, err.max()
+    mask = np.ones(P, bool)
+    mask[inp.rows] = False
+    assert (lat[mask] == 0x7F).all() and np.isnan(scales.cpu().numpy()[mask]).all()
+    if split_pools:
+        assert (rop[mask] == 0x7F).all() and (lat[inp.rows, 512:] == 0x7F).all()
