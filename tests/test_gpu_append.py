@@ -132,3 +132,64 @@ def test_kv_append_fp8_matches_oracle(n, d_model, split_pools):
     assert (lat[mask] == 0x7F).all() and np.isnan(scales.cpu().numpy()[mask]).all()
     if split_pools:
         assert (rop[mask] == 0x7F).all() and (lat[inp.rows, 512:] == 0x7F).all()
+
+
+def test_producer_rows_feed_the_decode_path():
+    """End to end: mla_kv_append writes every cached row of a small paged
+    batch (ragged lengths, permuted 64-token blocks), then the decode step
+    (absorb, split-K decode, combine + W_UV) attends over that pool.  The
+    oracle builds the same rows with kv_append and attends over them by the
+    non-absorbed definition; nothing on the reference side comes from the GPU.
+    Gate 2e-2 row-normwise (bf16 cache and queries)."""
+    from mla_inputs.generate import bf16_bits_from_f32
+    from tests._fake import ArrayInputs
+    from oracle import mla_decode
+
+    lens, H, d_model = [100, 64, 257], 16, 1024
+    B, n = len(lens), sum(lens)
+    app = AppendInputs(n, d_model, seed=20261230)
+    pos = np.concatenate([np.arange(L) for L in lens]).astype(np.int32)
+    nblk = [(L + 63) // 64 for L in lens]
+    perm = np.random.default_rng(5).permutation(sum(nblk))
+    mbps = max(nblk)
+    bt = np.full((B, mbps), -1, np.int32)
+    k = 0
+    for b in range(B):
+        bt[b, :nblk[b]] = perm[k:k + nblk[b]]
+        k += nblk[b]
+    rows = np.concatenate([bt[b][np.arange(L) // 64].astype(np.int64) * 64 + np.arange(L) % 64
+                           for b, L in enumerate(lens)])
+    dev = torch.device("cuda")
+    tb = lambda bits: torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+    pool = torch.full((sum(nblk) * 64, 576), NAN_BITS, dtype=torch.int16, device=dev).view(torch.bfloat16)
+    d_app = mla.append_dims(n, d_model)
+    ws = torch.empty(mla.mla_kv_append_workspace_bytes(d_app) // 4, dtype=torch.float32, device=dev)
+    mla.mla_kv_append(d_app, tb(app.h), tb(app.w_dkv), tb(app.kv_norm_w), tb(app.w_kr),
+                      torch.from_numpy(pos).to(dev), 10000.0, 1e-6, torch.from_numpy(rows).to(dev),
+                      pool, pool.view(-1)[512:].data_ptr(), 576, None, ws)
+
+    g = np.random.default_rng(6)
+    bits = lambda *s, sd=1.0: bf16_bits_from_f32((g.standard_normal(s) * sd).astype(np.float32))
+    qn, qr = bits(B, 1, H, 128), bits(B, 1, H, 64)
+    wuk, wuv = bits(H, 128, 512, sd=512 ** -0.5), bits(H, 128, 512, sd=512 ** -0.5)
+    qpos = np.array(lens, np.int32)[:, None]
+    d = mla.dims(B, 1, H, 128, 64, 512, 128, mla.BF16, mla.BF16)
+    step = mla.DecodeStep(d)
+    step.run(q_nope=tb(qn), q_rope=tb(qr), positions=torch.from_numpy(qpos).to(dev), w_uk=tb(wuk),
+             w_uv=tb(wuv), latent=pool, rope=pool[:, 512:], kv_row_stride=576, kv_scale=None,
+             seq_lens=torch.tensor(lens, dtype=torch.int32, device=dev),
+             block_table=torch.from_numpy(bt).to(dev), max_blocks_per_seq=mbps,
+             max_seq_len=max(lens), causal=False, softmax_scale=192 ** -0.5, rope_base=10000.0)
+    torch.cuda.synchronize()
+    got = step.o.float().cpu().numpy().astype(np.float64)
+
+    ckv, kr = kv_append(bf16_to_f64(app.h), bf16_to_f64(app.w_dkv), bf16_to_f64(app.kv_norm_w),
+                        bf16_to_f64(app.w_kr), pos, 10000.0, 1e-6)
+    rows64 = np.concatenate([ckv, kr], axis=1)
+    starts = np.cumsum([0] + lens)
+    inp = ArrayInputs(q_nope=bf16_to_f64(qn), q_rope=bf16_to_f64(qr), w_uk=bf16_to_f64(wuk),
+                      w_uv=bf16_to_f64(wuv), caches=[rows64[starts[b]:starts[b + 1]] for b in range(B)],
+                      positions=qpos)
+    want = mla_decode(inp)["o"]
+    err = np.abs(got - want).max(axis=-1) / np.abs(want).max(axis=-1)
+    assert err.max() < 2e-2, err.max()
