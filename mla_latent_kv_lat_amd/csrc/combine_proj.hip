@@ -132,8 +132,8 @@ __global__ __launch_bounds__(512) void combine_proj_kernel(
                  : unit_begin(u, T, G) < unit_begin(u + 1, T, G);
   };
 
-  // ---- phase 0b: the first loads of this wave's rows (clamped in range;
-  // what an empty unit holds is never used), then W_UV
+  // ---- phase 0b: the first loads of this wave's rows (what an empty unit
+  // holds is never used), then W_UV
   const int c = 8 * lane;  // latent columns of this lane in phase 1
   int64_t u0[kCPRowsPerWave], slot0[kCPRowsPerWave];
   int n[kCPRowsPerWave];
@@ -146,9 +146,11 @@ __global__ __launch_bounds__(512) void combine_proj_kernel(
     n[i] = __builtin_amdgcn_readfirstlane(row_n[j]);
     slot0[i] = uniform64(row_slot[j]);
     lv[i] = lse_part[slot0[i] + (int64_t)(lane < n[i] ? lane : 0) * R];
+    // only the units the row's sequence crossed (n is wave-uniform): the
+    // kernel is bound by the bytes each CU pulls in, so no duplicate loads
 #pragma unroll
     for (int k = 0; k < kCPChunk; ++k)
-      v[i][k] = *(const h8*)(o_part + (slot0[i] + (int64_t)(k < n[i] ? k : 0) * R) * 512 + c);
+      v[i][k] = k < n[i] ? *(const h8*)(o_part + (slot0[i] + (int64_t)k * R) * 512 + c) : h8{};
   }
   load_w();
 
