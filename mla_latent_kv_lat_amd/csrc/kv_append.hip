@@ -52,10 +52,20 @@ constexpr int kAppMaxChunks = 32;  // hidden width up to 16384 (API limit)
 __global__ __launch_bounds__(256) void kv_down_kernel(const uint16_t* __restrict__ h,
                                                       const uint16_t* __restrict__ w_dkv,
                                                       const uint16_t* __restrict__ w_kr,
-                                                      int n_tok, int d_model,
+                                                      int n_tok, int d_model, int n_chunks,
                                                       float* __restrict__ part) {
   __shared__ f32x4 red[3][2][4][64];
-  const int s = blockIdx.y;  // hidden columns [512 s, 512 s + 512)
+  // Work item p = (chunk s, channel block xb), chunk-major.  Workgroups are
+  // dealt to the 8 XCDs round-robin, so workgroup i takes item
+  // (i % 8) * per_xcd + i / 8: the channel blocks of one chunk then run on
+  // one or two XCDs and that chunk's hidden-state columns are fetched into
+  // one or two L2s instead of all eight.
+  const int n_items = (kAppN / 32) * n_chunks;
+  const int per_xcd = (n_items + 7) / 8;
+  const int p = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
+  if (p >= n_items) return;  // uniform across the workgroup
+  const int s = p / (kAppN / 32);   // hidden columns [512 s, 512 s + 512)
+  const int xb = p % (kAppN / 32);  // output channels 32 xb .. 32 xb + 31
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int li = lane & 15, g = lane >> 4;
   const int k0 = kAppChunk * s + 128 * w + 8 * g;
@@ -63,7 +73,7 @@ __global__ __launch_bounds__(256) void kv_down_kernel(const uint16_t* __restrict
   bf16x8 bw[2][4];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const int n = 32 * blockIdx.x + 16 * j + li;
+    const int n = 32 * xb + 16 * j + li;
     const uint16_t* wrow = n < kAppLat ? w_dkv + (int64_t)n * d_model
                                        : w_kr + (int64_t)(n - kAppLat) * d_model;
 #pragma unroll
@@ -98,7 +108,7 @@ __global__ __launch_bounds__(256) void kv_down_kernel(const uint16_t* __restrict
     if (w == 0) {
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const int n = 32 * blockIdx.x + 16 * j + li;
+        const int n = 32 * xb + 16 * j + li;
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) {
           const f32x4 t = acc[j][mb] + red[0][j][mb][lane] + red[1][j][mb][lane] + red[2][j][mb][lane];
@@ -253,9 +263,10 @@ int mla_kv_append(const mla_append_dims_t* dims, const void* h, const void* w_dk
   hipStream_t s = (hipStream_t)stream;
   (void)hipGetLastError();
   const int chunks = dims->d_model / kAppChunk;
-  hipLaunchKernelGGL(kv_down_kernel, dim3(kAppN / 32, chunks), dim3(256), 0, s,
+  const int items = (kAppN / 32) * chunks;
+  hipLaunchKernelGGL(kv_down_kernel, dim3(8 * ((items + 7) / 8)), dim3(256), 0, s,
                      (const uint16_t*)h, (const uint16_t*)w_dkv, (const uint16_t*)w_kr,
-                     dims->n_tokens, dims->d_model, (float*)workspace);
+                     dims->n_tokens, dims->d_model, chunks, (float*)workspace);
   if (hipGetLastError() != hipSuccess) return MLA_ERR_HIP;
   const dim3 fg((dims->n_tokens + 3) / 4);
   if (f8)
