@@ -21,7 +21,9 @@
 //                     operands have the contracted index contiguous, so
 //                     they load straight into MFMA registers; every weight
 //                     byte is read once.
-//   kv_finish_kernel  one wave per token: adds the chunks' partials,
+//   kv_finish_kernel  one single-wave workgroup per token (spreading the
+//                     partial loads over as many CUs as there are tokens):
+//                     adds the chunks' partials,
 //                     normalises the latent (mean square over 512 channels,
 //                     fp32), applies the norm weight, rotates the key at the
 //                     token's position (angle reduced in double precision),
@@ -127,13 +129,12 @@ __global__ __launch_bounds__(256) void kv_down_kernel(const uint16_t* __restrict
 // F8: e4m3 codes (OCP) of row / scale with scale = amax / 448 over the
 // token's 576 values, and the scale to kv_scale[row]; else bf16 values.
 template <bool F8>
-__global__ __launch_bounds__(256) void kv_finish_kernel(
+__global__ __launch_bounds__(64) void kv_finish_kernel(
     const float* __restrict__ part, int n_chunks, int n_tok, const uint16_t* __restrict__ w_norm,
     const int32_t* __restrict__ positions, double log2_base, float eps,
     const int64_t* __restrict__ rows, char* __restrict__ latent, char* __restrict__ rope,
     int64_t stride_bytes, float* __restrict__ kv_scale) {
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= n_tok) return;  // uniform per wave
+  const int t = blockIdx.x;  // one wave per token
   const int lane = threadIdx.x & 63;
   f32x4 v0 = f32x4{}, v1 = f32x4{};  // latent channels 8 lane .. 8 lane + 7
   float r0 = 0.f, r1 = 0.f;          // RoPE pair `lane` (lanes < 32)
@@ -268,14 +269,14 @@ int mla_kv_append(const mla_append_dims_t* dims, const void* h, const void* w_dk
                      (const uint16_t*)h, (const uint16_t*)w_dkv, (const uint16_t*)w_kr,
                      dims->n_tokens, dims->d_model, chunks, (float*)workspace);
   if (hipGetLastError() != hipSuccess) return MLA_ERR_HIP;
-  const dim3 fg((dims->n_tokens + 3) / 4);
+  const dim3 fg(dims->n_tokens);
   if (f8)
-    hipLaunchKernelGGL(kv_finish_kernel<true>, fg, dim3(256), 0, s, (const float*)workspace,
+    hipLaunchKernelGGL(kv_finish_kernel<true>, fg, dim3(64), 0, s, (const float*)workspace,
                        chunks, dims->n_tokens, (const uint16_t*)kv_norm_w, positions,
                        log2((double)rope_base), eps, cache_rows, (char*)latent_cache,
                        (char*)rope_cache, kv_row_stride, kv_scale);
   else
-    hipLaunchKernelGGL(kv_finish_kernel<false>, fg, dim3(256), 0, s, (const float*)workspace,
+    hipLaunchKernelGGL(kv_finish_kernel<false>, fg, dim3(64), 0, s, (const float*)workspace,
                        chunks, dims->n_tokens, (const uint16_t*)kv_norm_w, positions,
                        log2((double)rope_base), eps, cache_rows, (char*)latent_cache,
                        (char*)rope_cache, kv_row_stride * 2, nullptr);
