@@ -665,6 +665,9 @@ __global__ __launch_bounds__(512, 1) void decode_hs_kernel(DecodeArgs a) {
               __builtin_amdgcn_sched_barrier(0);
             }
           }
+          // the RoPE block's load first, the eight latent blocks' between the
+          // MFMAs (all nine at the top, or two per MFMA slot, measured slower)
+          if (more) issue_cg(plan, w, 8);
           const int lv = fresh_lane();
           const uint32_t o_pr = off_pr(lv);
           const uint32_t o_pv0 = off_pv(lv, 2 * c, 0), o_pv1 = off_pv(lv, 2 * c, 1);
@@ -687,7 +690,7 @@ __global__ __launch_bounds__(512, 1) void decode_hs_kernel(DecodeArgs a) {
               __builtin_amdgcn_sched_barrier(0);
             }
           }
-          issued = more ? 8 : 9;
+          issued = 9;
         }
         const bool last = j + 1 >= nsub || (chh == 1 && ci.rem <= kTile);
         if (last) {  // end of this unit's part of the sequence: write the partial
