@@ -105,6 +105,12 @@ CONFIGS = {
     "dsv3_b64_l8k_paged": MLAConfig(
         name="dsv3_b64_l8k_paged", batch=64, q_len=1, seq_len=8192,
         paged=True, seed=20261208, **_DSV3),
+    # Multi-token decode on the headline shape (two new tokens per sequence,
+    # e.g. one speculative or multi-token-prediction draft): both queries are
+    # in the cache and the second also sees the first (causal).
+    "dsv3_b64_l8k_paged_mtp2": MLAConfig(
+        name="dsv3_b64_l8k_paged_mtp2", batch=64, q_len=2, seq_len=8192,
+        paged=True, causal=True, query_in_cache=True, seed=20261209, **_DSV3),
 }
 
 HEADLINE = "dsv3_b64_l8k_paged"

@@ -21,7 +21,7 @@ from tests.test_gpu_parity import check_all_stages, run_gpu
 pytestmark = pytest.mark.gpu
 
 FULL = ["dsv3_b16_l4k", "dsv3_b64_ragged_paged", "dsv3_b64_l8k_paged", "long_b4_l128k",
-        "fp8_b128_l16k_q2"]
+        "fp8_b128_l16k_q2", "dsv3_b64_l8k_paged_mtp2"]
 
 
 def sample_rows(inp):
