@@ -37,9 +37,7 @@ using namespace mfma;
 
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 
-constexpr int kCPRows = 32;
 constexpr int kCPWaves = 8;
-constexpr int kCPRowsPerWave = kCPRows / kCPWaves;
 constexpr int kCPPitch = 1040;  // bytes per bf16 o_lat row in LDS: 1024 + 16 (conflict-free A reads)
 constexpr int kCPChunk = 4;     // partials per row loaded per pass
 
@@ -47,20 +45,22 @@ __device__ inline float lane_value(float v, int k) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), k));
 }
 
+template <int ROWS>
 __global__ __launch_bounds__(512) void combine_proj_kernel(
     int B, int Lq, int H, int G, const int32_t* __restrict__ seq_lens,
     const _Float16* __restrict__ o_part, const float* __restrict__ lse_part,
     const uint16_t* __restrict__ w_uv, int d_v, uint16_t* __restrict__ o,
     float* __restrict__ lse_out, uint16_t* __restrict__ o_lat) {
-  __shared__ __attribute__((aligned(16))) char lat[kCPRows * kCPPitch];
+  __shared__ __attribute__((aligned(16))) char lat[ROWS * kCPPitch];
   __shared__ __attribute__((aligned(16))) float red[4 * 64 * 16];
-  __shared__ int64_t row_u0[kCPRows], row_slot[kCPRows];
-  __shared__ int row_n[kCPRows];
+  __shared__ int64_t row_u0[ROWS], row_slot[ROWS];
+  __shared__ int row_n[ROWS];
   __shared__ int64_t tot_T;
 
+  constexpr int kRowsPerWave = ROWS / kCPWaves;
   const int h = blockIdx.x;
   const int M = B * Lq, R = Lq * H;
-  const int mb0 = blockIdx.y * kCPRows;
+  const int mb0 = blockIdx.y * ROWS;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int cq = w & 3, kh = w >> 2;
@@ -80,7 +80,7 @@ __global__ __launch_bounds__(512) void combine_proj_kernel(
   // (lane j) its sequence's first split unit u0, unit count n and first
   // partial slot (u0 + b) R + r
   const int b_lo = mb0 / Lq;
-  const int nb = mb0 < M ? (min(M, mb0 + kCPRows) - 1) / Lq - b_lo + 1 : 0;  // <= 32
+  const int nb = mb0 < M ? (min(M, mb0 + ROWS) - 1) / Lq - b_lo + 1 : 0;  // <= ROWS <= 64
   if (w == 0) {
     int64_t tot = 0, before = 0;
 #pragma unroll 4
@@ -92,7 +92,7 @@ __global__ __launch_bounds__(512) void combine_proj_kernel(
     const int64_t mine = lane < nb ? tiles_of(seq_lens[b_lo + lane]) : 0;
     int64_t incl = mine;
 #pragma unroll
-    for (int d = 1; d < 32; d <<= 1) {
+    for (int d = 1; d < 64; d <<= 1) {  // inclusive prefix over up to 64 sequences
       const int64_t x = __shfl_up(incl, d, 64);
       if (lane >= d) incl += x;
     }
@@ -104,7 +104,7 @@ __global__ __launch_bounds__(512) void combine_proj_kernel(
     const int64_t pb_mine = before + incl - mine;  // first tile of sequence b_lo + lane
     // lane j: row m = mb0 + j
     const int m = mb0 + lane;
-    const bool live = lane < kCPRows && m < M;
+    const bool live = lane < ROWS && m < M;
     const int b = live ? m / Lq : b_lo;
     const int64_t pb = __shfl(pb_mine, b - b_lo, 64), tb = __shfl(mine, b - b_lo, 64);
     int64_t u0 = 0;
@@ -113,7 +113,7 @@ __global__ __launch_bounds__(512) void combine_proj_kernel(
       u0 = unit_of_tile(pb, tot, G);
       n = (int)(unit_of_tile(pb + tb - 1, tot, G) - u0 + 1);
     }
-    if (lane < kCPRows) {
+    if (lane < ROWS) {
       row_u0[lane] = u0;
       row_n[lane] = n;
       row_slot[lane] = (u0 + b) * R + (live ? (m % Lq) * H + h : h);
@@ -135,12 +135,12 @@ __global__ __launch_bounds__(512) void combine_proj_kernel(
   // ---- phase 0b: the first loads of this wave's rows (what an empty unit
   // holds is never used), then W_UV
   const int c = 8 * lane;  // latent columns of this lane in phase 1
-  int64_t u0[kCPRowsPerWave], slot0[kCPRowsPerWave];
-  int n[kCPRowsPerWave];
-  float lv[kCPRowsPerWave];
-  h8 v[kCPRowsPerWave][kCPChunk];
+  int64_t u0[kRowsPerWave], slot0[kRowsPerWave];
+  int n[kRowsPerWave];
+  float lv[kRowsPerWave];
+  h8 v[kRowsPerWave][kCPChunk];
 #pragma unroll
-  for (int i = 0; i < kCPRowsPerWave; ++i) {
+  for (int i = 0; i < kRowsPerWave; ++i) {
     const int j = w + kCPWaves * i;
     u0[i] = uniform64(row_u0[j]);
     n[i] = __builtin_amdgcn_readfirstlane(row_n[j]);
@@ -156,7 +156,7 @@ __global__ __launch_bounds__(512) void combine_proj_kernel(
 
   // ---- phase 0c / 1: LSE, weights, weighted sum of the partials
 #pragma unroll
-  for (int i = 0; i < kCPRowsPerWave; ++i) {
+  for (int i = 0; i < kRowsPerWave; ++i) {
     const int j = w + kCPWaves * i, m = mb0 + j;
     const int ni = n[i];
     // empty units wrote no partial (weight 0); a row may span more than 64 units
@@ -228,37 +228,39 @@ __global__ __launch_bounds__(512) void combine_proj_kernel(
 #pragma unroll
       for (int k = 0; k < 16; ++k) bw[k] = bp[2 * (16 * kh + k) + hf];
     }
-    f32x16 acc2[2] = {f32x16{}, f32x16{}};  // even / odd k-steps: two chains
-    if (act) {
+    for (int rb = 0; rb < ROWS / 32; ++rb) {  // 32-row blocks of the tile
+      f32x16 acc2[2] = {f32x16{}, f32x16{}};  // even / odd k-steps: two chains
+      if (act) {
 #pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const bf16x8 av =
-            *(const bf16x8*)(lat + n32 * kCPPitch + (16 * (16 * kh + k) + 8 * hf) * 2);
-        acc2[k & 1] = mfma32(av, bw[k], acc2[k & 1]);
+        for (int k = 0; k < 16; ++k) {
+          const bf16x8 av = *(const bf16x8*)(lat + (32 * rb + n32) * kCPPitch +
+                                             (16 * (16 * kh + k) + 8 * hf) * 2);
+          acc2[k & 1] = mfma32(av, bw[k], acc2[k & 1]);
+        }
       }
+      mfma_settle(acc2[0]);
+      mfma_settle(acc2[1]);
+      f32x16 acc = acc2[0] + acc2[1];
+      f32x4* rp = (f32x4*)(red + (cq * 64 + lane) * 16);
+      if (kh == 1 && act)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) rp[q] = f32x4{acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
+      __syncthreads();
+      if (kh == 0 && act) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 t = rp[q];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[4 * q + e] += t[e];
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int mr = mb0 + 32 * rb + 8 * (r >> 2) + 4 * hf + (r & 3);
+          if (mr < M) o[((int64_t)mr * H + h) * d_v + 32 * cb + n32] = f32_to_bf16(acc[r]);
+        }
+      }
+      __syncthreads();
     }
-    mfma_settle(acc2[0]);
-    mfma_settle(acc2[1]);
-    f32x16 acc = acc2[0] + acc2[1];
-    f32x4* rp = (f32x4*)(red + (cq * 64 + lane) * 16);
-    if (kh == 1 && act)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) rp[q] = f32x4{acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
-    __syncthreads();
-    if (kh == 0 && act) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const f32x4 t = rp[q];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[4 * q + e] += t[e];
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int mr = mb0 + 8 * (r >> 2) + 4 * hf + (r & 3);
-        if (mr < M) o[((int64_t)mr * H + h) * d_v + 32 * cb + n32] = f32_to_bf16(acc[r]);
-      }
-    }
-    __syncthreads();
   }
 }
 
@@ -272,8 +274,18 @@ hipError_t launch_combine_proj(const mla_dims_t& d, int num_splits, const int32_
                                const void* o_part, const float* lse_part, const void* w_uv,
                                void* o, float* lse_out, void* o_lat, hipStream_t s) {
   const int M = d.batch * d.q_len;
-  dim3 grid((unsigned)d.heads, (unsigned)((M + kCPRows - 1) / kCPRows));
-  hipLaunchKernelGGL(combine_proj_kernel, grid, dim3(512), 0, s, d.batch, d.q_len, d.heads,
+  // 32 query rows per workgroup up to 64 rows (every CU busy), 64 from 128
+  // rows on: the workgroup holds one CU, so fewer, larger ones halve the
+  // rounds of workgroups and the re-reads of W_UV[h]
+  if (M >= 128) {
+    dim3 grid((unsigned)d.heads, (unsigned)((M + 63) / 64));
+    hipLaunchKernelGGL(combine_proj_kernel<64>, grid, dim3(512), 0, s, d.batch, d.q_len, d.heads,
+                       num_splits, seq_lens, (const _Float16*)o_part, lse_part,
+                       (const uint16_t*)w_uv, d.d_v, (uint16_t*)o, lse_out, (uint16_t*)o_lat);
+    return hipGetLastError();
+  }
+  dim3 grid((unsigned)d.heads, (unsigned)((M + 31) / 32));
+  hipLaunchKernelGGL(combine_proj_kernel<32>, grid, dim3(512), 0, s, d.batch, d.q_len, d.heads,
                      num_splits, seq_lens, (const _Float16*)o_part, lse_part,
                      (const uint16_t*)w_uv, d.d_v, (uint16_t*)o, lse_out, (uint16_t*)o_lat);
   return hipGetLastError();

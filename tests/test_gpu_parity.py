@@ -192,9 +192,12 @@ def test_bf16_mfma_32_heads_and_empty_sequence():
 
 # ------------------------------------------------ fused combine + W_UV
 
-@pytest.mark.parametrize("q_len,causal", [(1, False), (2, True)])
-def test_combine_out_proj_matches_two_calls(q_len, causal):
-    cfg = scaled(BF16_RAGGED, batch=5, heads=64, paged=True, q_len=q_len, causal=causal,
+# batch 130 / 70: 130 and 140 query rows, where the fused kernel takes 64 rows
+# per workgroup (64 and 32 sequences per block)
+@pytest.mark.parametrize("q_len,causal,batch", [(1, False, 5), (2, True, 5), (1, False, 130),
+                                                (2, True, 70)])
+def test_combine_out_proj_matches_two_calls(q_len, causal, batch):
+    cfg = scaled(BF16_RAGGED, batch=batch, heads=64, paged=True, q_len=q_len, causal=causal,
                  query_in_cache=causal)
     inp = MLAInputs(cfg)
     dev = to_device(inp)
