@@ -66,8 +66,7 @@ __global__ __launch_bounds__(512) void combine_proj_kernel(
   const int cq = w & 3, kh = w >> 2;
   const int hf = lane >> 5, n32 = lane & 31;
 
-  // W_UV[h] rows 32 cq + n32, latent half kh: loaded after the partials
-  // (needed first), in flight during phases 0-1
+  // W_UV[h] rows 32 cq + n32, latent half kh: in flight during phase 1
   bf16x8 bw[16];
   auto load_w = [&]() {
     const int vb = 32 * cq;
@@ -75,8 +74,15 @@ __global__ __launch_bounds__(512) void combine_proj_kernel(
 #pragma unroll
     for (int k = 0; k < 16; ++k) bw[k] = bp[2 * (16 * kh + k) + hf];
   };
+  // With 32 rows the weights go out first: waves 1-7 start their loads
+  // while wave 0 works out the rows' units (then issues its own), so the
+  // CU's inflow is busy through that pass (19.8 -> 19.2 us at 64 sequences).
+  // With 64 rows the partials are twice the bytes and must not queue behind
+  // the weights (measured 53.4 -> 57.4 us at 256 rows), so they go first.
+  constexpr bool kWeightsFirst = ROWS <= 32;
+  if (kWeightsFirst && w != 0) load_w();
 
-  // ---- phase 0a, by wave 0: total tiles T, then for each of the 32 rows
+  // ---- phase 0a, by wave 0: total tiles T, then for each of the rows
   // (lane j) its sequence's first split unit u0, unit count n and first
   // partial slot (u0 + b) R + r
   const int b_lo = mb0 / Lq;
@@ -119,8 +125,9 @@ __global__ __launch_bounds__(512) void combine_proj_kernel(
       row_slot[lane] = (u0 + b) * R + (live ? (m % Lq) * H + h : h);
     }
     if (lane == 0) tot_T = tot;
+    if (kWeightsFirst) load_w();
   }
-  __syncthreads();
+  block_sync();  // no wait on the weight loads in flight
   const int64_t T = tot_T;
   // with G <= T no unit is empty
   const bool may_be_empty = G > T;
@@ -152,7 +159,7 @@ __global__ __launch_bounds__(512) void combine_proj_kernel(
     for (int k = 0; k < kCPChunk; ++k)
       v[i][k] = k < n[i] ? *(const h8*)(o_part + (slot0[i] + (int64_t)k * R) * 512 + c) : h8{};
   }
-  load_w();
+  if (!kWeightsFirst) load_w();
 
   // ---- phase 0c / 1: LSE, weights, weighted sum of the partials
 #pragma unroll

@@ -168,6 +168,22 @@ def test_fp8_mfma_ragged_causal(paged, splits):
     check_all_stages(inp, run_gpu(inp, num_splits=splits))
 
 
+# More than two draft tokens per sequence (multi-token prediction or
+# speculative decoding): 3 and 4 causal queries, 384 and 512 query rows over
+# 128 heads, the shortest sequence holding just its queries.
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+@pytest.mark.parametrize("q_len", [3, 4])
+@pytest.mark.parametrize("splits", [1, 7])
+def test_mfma_multi_token_causal(kv, q_len, splits):
+    base = BF16_RAGGED if kv == "bf16" else FP8_RAGGED
+    cfg = scaled(base, paged=True, q_len=q_len, causal=True, query_in_cache=True, len_lo=q_len,
+                 seed=base.seed + q_len)
+    inp = MLAInputs(cfg)
+    inp.seq_lens[0] = q_len
+    inp.positions[0] = np.arange(q_len)
+    check_all_stages(inp, run_gpu(inp, num_splits=splits))
+
+
 def test_fp8_mfma_matches_generic_kernels():
     inp = MLAInputs(scaled(FP8_RAGGED, paged=True, seed=77))
     dev = to_device(inp)
