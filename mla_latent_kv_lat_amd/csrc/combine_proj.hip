@@ -6,8 +6,8 @@
 //          DeepSeek MLA Matrix Absorption and Memory Minimalism"
 //   [MATH] "Multi-Head Latent Attention (MLA): Mathematical Foundations, ..."
 //
-// One workgroup of 8 waves per (head h, 32 query rows m = (b, i)); wave w
-// owns rows w, w + 8, w + 16, w + 24 in phases 0-1:
+// One workgroup of 8 waves per (head h, 32 or 64 query rows m = (b, i));
+// wave w owns rows w, w + 8, w + 16, ... in phases 0-1:
 //   phase 0  the split-K units that touched each row's sequence b (from one
 //            prefix pass over seq_lens per workgroup) and the log-sum-exp of
 //            their partials, lse = log sum_u exp(lse_u); lane k of the wave
@@ -20,7 +20,10 @@
 //   phase 2  o = o_lat W_UV[h]^T on v_mfma_f32_32x32x16_bf16 ([ARCH] 3.2):
 //            wave w takes the 32 v-columns 32 (w & 3) + 128 j and half w >> 2
 //            of the 512 latent columns, with its rows of W_UV[h] loaded into
-//            registers at the start; the two halves meet in LDS.
+//            registers early; the two halves meet in LDS.  When two
+//            workgroups share a head (all rows in one block), each takes two
+//            of every four 32-column blocks and a wave a quarter of the
+//            latent columns; the four quarters meet in LDS.
 // The latent output never makes an HBM round trip between the two steps.
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -45,14 +48,20 @@ __device__ inline float lane_value(float v, int k) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), k));
 }
 
-template <int ROWS>
+// ROWS query rows per workgroup; VS workgroups (blockIdx.z = vpart) share a head's
+// v-columns when one row block holds every row, so that W_UV[h] is pulled
+// into VS CUs in parts instead of into one CU whole.  Each of them combines
+// the same rows (the partials are read VS times).
+template <int ROWS, int VS>
 __global__ __launch_bounds__(512) void combine_proj_kernel(
     int B, int Lq, int H, int G, const int32_t* __restrict__ seq_lens,
     const _Float16* __restrict__ o_part, const float* __restrict__ lse_part,
     const uint16_t* __restrict__ w_uv, int d_v, uint16_t* __restrict__ o,
     float* __restrict__ lse_out, uint16_t* __restrict__ o_lat) {
   __shared__ __attribute__((aligned(16))) char lat[ROWS * kCPPitch];
-  __shared__ __attribute__((aligned(16))) float red[4 * 64 * 16];
+  // v-column blocks per pass and latent parts per block: 4 x 2 or 2 x 4 waves
+  constexpr int kNC = 4 / VS, kNK = kCPWaves / kNC, kSteps = 32 / kNK;
+  __shared__ __attribute__((aligned(16))) float red[(kNK - 1) * kNC * 64 * 16];
   __shared__ int64_t row_u0[ROWS], row_slot[ROWS];
   __shared__ int row_n[ROWS];
   __shared__ int64_t tot_T;
@@ -63,16 +72,18 @@ __global__ __launch_bounds__(512) void combine_proj_kernel(
   const int mb0 = blockIdx.y * ROWS;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int cq = w & 3, kh = w >> 2;
+  const int vpart = blockIdx.z;  // which of the VS workgroups of this head
+  const int cq = w % kNC, kh = w / kNC;
   const int hf = lane >> 5, n32 = lane & 31;
 
-  // W_UV[h] rows 32 cq + n32, latent half kh: in flight during phase 1
-  bf16x8 bw[16];
+  // W_UV[h] rows 32 (kNC vpart + cq) + n32, latent part kh: in flight during
+  // phase 1
+  bf16x8 bw[kSteps];
   auto load_w = [&]() {
-    const int vb = 32 * cq;
+    const int vb = 32 * (kNC * vpart + cq);
     const bf16x8* bp = (const bf16x8*)(w_uv + ((int64_t)h * d_v + (vb < d_v ? vb : 0) + n32) * 512);
 #pragma unroll
-    for (int k = 0; k < 16; ++k) bw[k] = bp[2 * (16 * kh + k) + hf];
+    for (int k = 0; k < kSteps; ++k) bw[k] = bp[2 * (kSteps * kh + k) + hf];
   };
   // With 32 rows the weights go out first: waves 1-7 start their loads
   // while wave 0 works out the rows' units (then issues its own), so the
@@ -182,7 +193,7 @@ __global__ __launch_bounds__(512) void combine_proj_kernel(
     z = wave_sum(z);
     const float lse = mx == -INFINITY ? -INFINITY : mx + logf(z);
     const float wt = (lse != -INFINITY && x != -INFINITY) ? expf(x - lse) : 0.f;
-    if (lse_out && m < M && lane == 0) lse_out[(int64_t)m * H + h] = lse;
+    if (lse_out && vpart == 0 && m < M && lane == 0) lse_out[(int64_t)m * H + h] = lse;
 
     float acc[8];
 #pragma unroll
@@ -220,45 +231,50 @@ __global__ __launch_bounds__(512) void combine_proj_kernel(
 #pragma unroll
     for (int e = 0; e < 8; ++e) ov[e] = (__bf16)acc[e];
     *(bf16x8*)(lat + j * kCPPitch + 16 * lane) = ov;  // rows past M hold zeros
-    if (o_lat && m < M) *(bf16x8*)(o_lat + ((int64_t)m * H + h) * 512 + c) = ov;
+    if (o_lat && vpart == 0 && m < M) *(bf16x8*)(o_lat + ((int64_t)m * H + h) * 512 + c) = ov;
   }
   __syncthreads();
 
   // ---- phase 2: o[m, h, vb..vb+31] = o_lat[m] W_UV[h][vb..]^T; the wave sums
-  // latent half kh, half 1 hands its sums to half 0 through LDS
+  // latent part kh, parts 1.. hand their sums to part 0 through LDS
   const int nvb = d_v / 32;
   for (int base = 0; base < nvb; base += 4) {
-    const int cb = base + cq;
+    const int cb = base + kNC * vpart + cq;
     const bool act = cb < nvb;
     if (base > 0 && act) {
       const bf16x8* bp = (const bf16x8*)(w_uv + ((int64_t)h * d_v + 32 * cb + n32) * 512);
 #pragma unroll
-      for (int k = 0; k < 16; ++k) bw[k] = bp[2 * (16 * kh + k) + hf];
+      for (int k = 0; k < kSteps; ++k) bw[k] = bp[2 * (kSteps * kh + k) + hf];
     }
     for (int rb = 0; rb < ROWS / 32; ++rb) {  // 32-row blocks of the tile
       f32x16 acc2[2] = {f32x16{}, f32x16{}};  // even / odd k-steps: two chains
       if (act) {
 #pragma unroll
-        for (int k = 0; k < 16; ++k) {
+        for (int k = 0; k < kSteps; ++k) {
           const bf16x8 av = *(const bf16x8*)(lat + (32 * rb + n32) * kCPPitch +
-                                             (16 * (16 * kh + k) + 8 * hf) * 2);
+                                             (16 * (kSteps * kh + k) + 8 * hf) * 2);
           acc2[k & 1] = mfma32(av, bw[k], acc2[k & 1]);
         }
       }
       mfma_settle(acc2[0]);
       mfma_settle(acc2[1]);
       f32x16 acc = acc2[0] + acc2[1];
-      f32x4* rp = (f32x4*)(red + (cq * 64 + lane) * 16);
-      if (kh == 1 && act)
+      if (kh >= 1 && act) {
+        f32x4* rp = (f32x4*)(red + (((kh - 1) * kNC + cq) * 64 + lane) * 16);
 #pragma unroll
         for (int q = 0; q < 4; ++q) rp[q] = f32x4{acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
+      }
       __syncthreads();
       if (kh == 0 && act) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const f32x4 t = rp[q];
+        for (int p = 1; p < kNK; ++p) {
+          const f32x4* rp = (const f32x4*)(red + (((p - 1) * kNC + cq) * 64 + lane) * 16);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) acc[4 * q + e] += t[e];
+          for (int q = 0; q < 4; ++q) {
+            const f32x4 t = rp[q];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[4 * q + e] += t[e];
+          }
         }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -283,18 +299,25 @@ hipError_t launch_combine_proj(const mla_dims_t& d, int num_splits, const int32_
   const int M = d.batch * d.q_len;
   // 32 query rows per workgroup up to 64 rows (every CU busy), 64 from 128
   // rows on: the workgroup holds one CU, so fewer, larger ones halve the
-  // rounds of workgroups and the re-reads of W_UV[h]
+  // rounds of workgroups and the re-reads of W_UV[h].  Up to 32 rows one
+  // workgroup per head would leave half the CUs idle: two share its
+  // v-columns.
   if (M >= 128) {
     dim3 grid((unsigned)d.heads, (unsigned)((M + 63) / 64));
-    hipLaunchKernelGGL(combine_proj_kernel<64>, grid, dim3(512), 0, s, d.batch, d.q_len, d.heads,
+    hipLaunchKernelGGL((combine_proj_kernel<64, 1>), grid, dim3(512), 0, s, d.batch, d.q_len, d.heads,
                        num_splits, seq_lens, (const _Float16*)o_part, lse_part,
                        (const uint16_t*)w_uv, d.d_v, (uint16_t*)o, lse_out, (uint16_t*)o_lat);
-    return hipGetLastError();
+  } else if (M > 32) {
+    dim3 grid((unsigned)d.heads, (unsigned)((M + 31) / 32));
+    hipLaunchKernelGGL((combine_proj_kernel<32, 1>), grid, dim3(512), 0, s, d.batch, d.q_len, d.heads,
+                       num_splits, seq_lens, (const _Float16*)o_part, lse_part,
+                       (const uint16_t*)w_uv, d.d_v, (uint16_t*)o, lse_out, (uint16_t*)o_lat);
+  } else {
+    dim3 grid((unsigned)d.heads, 1u, 2u);
+    hipLaunchKernelGGL((combine_proj_kernel<32, 2>), grid, dim3(512), 0, s, d.batch, d.q_len, d.heads,
+                       num_splits, seq_lens, (const _Float16*)o_part, lse_part,
+                       (const uint16_t*)w_uv, d.d_v, (uint16_t*)o, lse_out, (uint16_t*)o_lat);
   }
-  dim3 grid((unsigned)d.heads, (unsigned)((M + 31) / 32));
-  hipLaunchKernelGGL(combine_proj_kernel<32>, grid, dim3(512), 0, s, d.batch, d.q_len, d.heads,
-                     num_splits, seq_lens, (const _Float16*)o_part, lse_part,
-                     (const uint16_t*)w_uv, d.d_v, (uint16_t*)o, lse_out, (uint16_t*)o_lat);
   return hipGetLastError();
 }
 
