@@ -11,9 +11,12 @@ all on one stream.
 The default workload is DeepSeek-V3 shaped: batch 64, 8192 cached tokens per
 sequence, 128 heads, latent 512 + RoPE 64, bf16, paged in 64-token blocks.
 
-The default warmup (500 steps, ~0.1 s) lets the GPU clock settle at its
-sustained level before the timed steps; with only a few warmup steps the
-timed region falls inside the clock ramp and reads up to ~25% slower.
+After the --warmup steps a settle phase of sustained steps (--settle-ms,
+default 300 ms, reported as settle_ms) lets the GPU clock reach its steady
+level; a timed region inside the clock ramp reads up to ~25% slower.  The
+timed steps rotate over copies of the inputs (one per model layer, enough of
+them to exceed the 256 MB Infinity Cache three times), each step one HIP
+graph replay with its own events; ms_per_step is the median step.
 
 Prints one JSON line on stdout.  `value` is cache GB/s of the whole step
 (cached bytes / step time); `ms_per_step` gives the step latency.  The
@@ -34,6 +37,7 @@ import numpy as np
 
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0      # dense bf16 MFMA
+INFINITY_CACHE_BYTES = 256 * 2**20
 METRIC = "MLA decode µs/step, TFLOP/s and cache GB/s at B=64,L=8k,128 heads (% roofline)"
 
 
@@ -55,6 +59,22 @@ def accounting(inp):
     proj_flops = 2.0 * B * Lq * H * (c.d_nope * c.d_latent + c.d_latent * c.d_v)
     return dict(tokens=tokens, cache_bytes=cache, step_bytes=cache + w + q + o,
                 attn_flops=attn_flops, step_flops=attn_flops + proj_flops)
+
+
+def clone_inputs(run_args: dict) -> dict:
+    """A device copy of a step's inputs (a further layer): the cache pool,
+    weights and queries are duplicated; the latent and RoPE views keep their
+    offsets into the copied pool; sizes and scalars are shared."""
+    out = dict(run_args)
+    lat, rop = run_args["latent"], run_args["rope"]
+    pool = lat.as_strided((lat.untyped_storage().nbytes() // lat.element_size(),), (1,), 0)
+    pool2 = pool.clone()
+    out["latent"] = pool2.as_strided(lat.shape, lat.stride(), lat.storage_offset())
+    out["rope"] = pool2.as_strided(rop.shape, rop.stride(), rop.storage_offset())
+    for k in ("q_nope", "q_rope", "w_uk", "w_uv", "kv_scale"):
+        if run_args[k] is not None:
+            out[k] = run_args[k].clone()
+    return out
 
 
 def cpu_baseline(inp, seconds: float):
@@ -87,10 +107,12 @@ def cpu_baseline(inp, seconds: float):
     dt = timed(sample)
     acc = accounting(inp)
     frac = n / len(rows_all)
-    threads = max([t.get("num_threads", 1) for t in threadpool_info()] or [1])
+    blas = max([t.get("num_threads", 1) for t in threadpool_info()] or [1])
+    cores = len(os.sched_getaffinity(0))
     seqs = sorted(set(r[0] for r in sample))
     return {"value": round(frac * acc["cache_bytes"] / dt / 1e9, 4), "unit": "GB/s",
-            "cores": int(threads), "kind": "oracle",
+            "cores": int(min(blas, cores)), "host_cpus": cores, "os_cpu_count": os.cpu_count(),
+            "blas_threads": int(blas), "kind": "oracle",
             "sample": f"{n} of {len(rows_all)} (b,i,h) query rows (sequences {seqs[0]}..{seqs[-1]}), "
                       f"{dt:.1f} s; value = the sample's share of the step's cache bytes / time"}
 
@@ -145,16 +167,21 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     # the GPU clock takes ~100 ms of sustained load to reach its steady
-    # level; the default warmup covers that, so the timed steps measure the
-    # sustained rate of a decode loop rather than the ramp
+    # level; the settle phase after the warmup covers that whatever --warmup
+    # says, so the timed steps measure the sustained rate of a decode loop
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--num-splits", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--append-d-model", type=int, default=7168,
                     help="hidden width of the cache-append producer timed beside the step")
     ap.add_argument("--cpu-seconds", type=float, default=25.0)
+    ap.add_argument("--settle-ms", type=float, default=300.0,
+                    help="untimed sustained steps after the warmup, so the clock is steady")
+    ap.add_argument("--layer-copies", type=int, default=0,
+                    help="input copies the steps rotate over (0: enough to exceed 3x the "
+                         "256 MB Infinity Cache)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -203,76 +230,105 @@ def main():
                     max_blocks_per_seq=dev.max_blocks_per_seq, max_seq_len=dev.max_seq_len,
                     causal=dev.causal, softmax_scale=dev.softmax_scale, rope_base=dev.rope_base)
 
-    def absorb():
-        mla.mla_absorb_q(d, dev.q_nope, dev.q_rope, dev.positions, dev.rope_base, dev.w_uk,
-                         step.q_abs, stream)
-
-    def decode():
-        mla.mla_decode_attn(d, step.q_abs, dev.latent, dev.rope, dev.kv_row_stride, dev.kv_scale,
-                            dev.seq_lens, dev.block_table, dev.max_blocks_per_seq,
-                            mla.TILE_TOKENS, dev.max_seq_len, dev.causal, dev.softmax_scale, G,
-                            step.o_part, step.lse_part, stream)
-
-    def combine_out_proj():
-        mla.mla_combine_out_proj(d, G, dev.seq_lens, step.o_part, step.lse_part, dev.w_uv, step.o,
-                                 step.lse, None, stream)
-
-    parts = [absorb, decode, combine_out_proj]
-
-    def timed(fn, k):
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for _ in range(k):
-            fn()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / k
-
-    for _ in range(args.warmup):
-        step.run(**args_run)
+    # ---- layer copies: the step's inputs (cache, weights, queries) are
+    # replicated and the timed steps rotate over them, as the layers of a
+    # model would, so that the working set of consecutive steps exceeds the
+    # 256 MB Infinity Cache at least three times over and steps are served
+    # from HBM, not from a cache that still holds the previous step's bytes
+    acc0 = accounting(inp)
+    part_bytes = step.o_part.numel() * step.o_part.element_size() + \
+        step.q_abs.numel() * step.q_abs.element_size()
+    ws_bytes = acc0["step_bytes"] + part_bytes
+    n_copies = max(1, -(-3 * INFINITY_CACHE_BYTES // ws_bytes)) if args.layer_copies <= 0 \
+        else args.layer_copies
+    copies = [args_run] + [clone_inputs(args_run) for _ in range(n_copies - 1)]
     torch.cuda.synchronize()
+
+    def run_copy(i):
+        step.run(**copies[i % n_copies])
+
+    # ---- warmup: the W steps asked for, then a settle phase of at least
+    # --settle-ms of sustained steps: the GPU clock needs ~0.1 s of load to
+    # reach its steady level, and a timed region inside the ramp reads up to
+    # 25% slow.  Both are untimed; the line reports the settle phase.
+    for i in range(args.warmup):
+        run_copy(i)
+    torch.cuda.synchronize()
+    t_settle = time.perf_counter()
+    settle_steps = 0
+    while (time.perf_counter() - t_settle) * 1e3 < args.settle_ms:
+        for _ in range(20):
+            run_copy(settle_steps)
+            settle_steps += 1
+        torch.cuda.synchronize()
+    settle_ms = (time.perf_counter() - t_settle) * 1e3
     if not torch.isfinite(step.o.float()).all():
         raise RuntimeError("non-finite decode output")
 
-    # ---- eager launches, then the same steps replayed from a HIP graph that
-    # holds several consecutive steps (as a model's layers would share one
-    # graph), so the per-replay launch cost is spread over them (measured in
-    # one process: ~1 us per step less than one step per graph)
-    ms_eager = timed(lambda: step.run(**args_run), args.steps)
-    spg = next(n for n in (10, 8, 5, 4, 2, 1) if args.steps % n == 0)
-    graph = step.capture(steps=spg, **args_run)
-    for _ in range(max(1, args.warmup // spg)):
-        graph.replay()
-    # ---- timed region: exactly K steps (K / spg graph replays on the same stream)
-    ms_step = timed(graph.replay, args.steps // spg) / spg
+    def timed_each(fn, k):
+        """Events on the stream before and after each of k calls: per-call
+        durations in ms and the whole region's."""
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(k + 1)]
+        torch.cuda.synchronize()
+        ev[0].record(stream)
+        for i in range(k):
+            fn(i)
+            ev[i + 1].record(stream)
+        torch.cuda.synchronize()
+        each = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(k)])
+        return each, ev[0].elapsed_time(ev[k])
+
+    # ---- eager launches, then the same steps replayed from HIP graphs (one
+    # per layer copy, one step each), which skip the host launch overhead
+    eager_each, _ = timed_each(run_copy, args.steps)
+    graphs = [step.capture(steps=1, **c) for c in copies]
+    t_settle = time.perf_counter()
+    i = 0
+    while (time.perf_counter() - t_settle) * 1e3 < args.settle_ms / 2:
+        for _ in range(20):
+            graphs[i % n_copies].replay()
+            i += 1
+        torch.cuda.synchronize()
+    # ---- timed region: exactly K steps, one graph replay each, bracketed by
+    # synchronisations; ms_per_step is the median step (the mean beside it)
+    step_each, region_ms = timed_each(lambda i: graphs[i % n_copies].replay(), args.steps)
+    ms_step = float(np.median(step_each))
+    step_pct = [round(float(np.percentile(step_each, q)) * 1e3, 2) for q in (10, 50, 90)]
 
     # ---- per-kernel durations (events around each launch, same stream)
+    def run_parts(i):
+        c = copies[i % n_copies]
+        return [lambda: mla.mla_absorb_q(d, c["q_nope"], c["q_rope"], c["positions"],
+                                         c["rope_base"], c["w_uk"], step.q_abs, stream),
+                lambda: mla.mla_decode_attn(d, step.q_abs, c["latent"], c["rope"],
+                                            c["kv_row_stride"], c["kv_scale"], c["seq_lens"],
+                                            c["block_table"], c["max_blocks_per_seq"],
+                                            mla.TILE_TOKENS, c["max_seq_len"], c["causal"],
+                                            c["softmax_scale"], G, step.o_part, step.lse_part,
+                                            stream),
+                lambda: mla.mla_combine_out_proj(d, G, c["seq_lens"], step.o_part, step.lse_part,
+                                                 c["w_uv"], step.o, step.lse, None, stream)]
+
+    n_parts = 3
     evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-            for _ in parts] for _ in range(args.steps)]
+            for _ in range(n_parts)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     for k in range(args.steps):
-        for f, (a, b) in zip(parts, evs[k]):
+        for f, (a, b) in zip(run_parts(k), evs[k]):
             a.record(stream)
             f()
             b.record(stream)
     torch.cuda.synchronize()
-    kern_ms = [float(np.mean([evs[k][j][0].elapsed_time(evs[k][j][1]) for k in range(args.steps)]))
-               for j in range(len(parts))]
-    # per-step spread from the same pass (first kernel's start to last kernel's end)
-    step_us = np.array([evs[k][0][0].elapsed_time(evs[k][-1][1]) for k in range(args.steps)]) * 1e3
-    step_pct = [round(float(np.percentile(step_us, q)), 2) for q in (10, 50, 90)]
+    kern_ms = [float(np.median([evs[k][j][0].elapsed_time(evs[k][j][1]) for k in range(args.steps)]))
+               for j in range(n_parts)]
 
     kv_app = append_pass(mla, stream, cfg.batch * cfg.q_len, args.append_d_model,
                          lambda: step.run(**args_run), min(args.steps, 100))
 
-    acc = accounting(inp)
-    # bytes a step touches: cache, weights, activations and the split-K workspaces; below the
-    # 256 MB Infinity Cache the repeated steps are served from it and the number is labelled
-    ws_bytes = acc["step_bytes"] + step.o_part.numel() * step.o_part.element_size() + \
-        step.q_abs.numel() * step.q_abs.element_size()
-    mall_hot = ws_bytes < 256 * 2**20
+    acc = acc0
+    # bytes the rotation touches before a copy comes round again: below the
+    # 256 MB Infinity Cache repeated steps would be served from it
+    mall_hot = ws_bytes * n_copies < INFINITY_CACHE_BYTES
     us_step = ms_step * 1e3
     cache_gbs = acc["cache_bytes"] / (ms_step * 1e-3) / 1e9
     tflops = acc["step_flops"] / (ms_step * 1e-3) / 1e12
@@ -307,8 +363,11 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5),
         "us_per_step": round(us_step, 2),
-        "eager_us_per_step": round(ms_eager * 1e3, 2),
+        "mean_us_per_step": round(region_ms / args.steps * 1e3, 2),
+        "eager_us_per_step": round(float(np.median(eager_each)) * 1e3, 2),
         "step_us_p10_p50_p90": step_pct,
+        "settle_ms": round(settle_ms, 1),
+        "settle_steps": settle_steps,
         "tflops": round(tflops, 2),
         "pct_roofline": round(100.0 * t_roof / (ms_step * 1e-3), 2),
         "higher_is_better": True,
@@ -322,8 +381,10 @@ def main():
                    "d_v": cfg.d_v, "paged_block": 64 if cfg.paged else 0,
                    "kv_dtype": cfg.kv_dtype, "num_splits": G, "parallelism": "single GPU",
                    "working_set_MB": round(ws_bytes / 1e6, 1),
+                   "layer_copies": n_copies,
                    "infinity_cache_hot": bool(mall_hot),
-                   "launch": f"HIP graph replay, {spg} steps of three kernels per graph (eager time beside)"},
+                   "launch": "HIP graph replay, one step of three kernels per replay, rotating over "
+                             "the layer copies; median step (eager time beside)"},
         "kernels_us": {"absorb_q": round(kern_ms[0] * 1e3, 2), "decode_attn": round(kern_ms[1] * 1e3, 2),
                        "combine_out_proj": round(kern_ms[2] * 1e3, 2)},
         "kv_append": kv_app,

@@ -24,3 +24,12 @@ def tol_for(cfg) -> float:
     if cfg.kv_dtype == "fp8":
         return TOL["fp8"]
     return TOL[cfg.q_dtype]
+
+
+# Per-stage errors of every parity case, printed in the terminal summary so
+# that the margins against the gates appear in the tail of a quiet run.
+RECORDED: list = []
+
+
+def record(label: str, errs: dict, tol: float) -> None:
+    RECORDED.append((label, dict(errs), float(tol)))

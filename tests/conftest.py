@@ -8,3 +8,21 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+
+
+def pytest_terminal_summary(terminalreporter, exitstatus, config):
+    """One line per parity case: the largest error of each stage and its
+    share of the gate (q_lat, q_pe, o_lat, o row-normwise; lse absolute)."""
+    from tests._metrics import RECORDED
+
+    if not RECORDED:
+        return
+    tr = terminalreporter
+    tr.section("parity margins (max error per stage / gate)")
+    worst = 0.0
+    for label, errs, tol in RECORDED:
+        frac = max(errs.values()) / tol if errs else 0.0
+        worst = max(worst, frac)
+        tr.write_line(f"{label}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items())
+                      + f" gate={tol:.0e} worst={frac:.2f}")
+    tr.write_line(f"{len(RECORDED)} cases, largest error / gate = {worst:.2f}")

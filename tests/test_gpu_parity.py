@@ -7,6 +7,8 @@ with the non-absorbed definition.  Gates (row-normwise max relative error):
 1e-5 fp32, 2e-2 bf16, 5e-2 fp8 cache.
 """
 
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -15,7 +17,7 @@ import mla_latent_kv_lat_amd as mla
 from mla_inputs import CONFIGS, MLAInputs, scaled
 from mla_inputs.device import to_device
 from oracle import mla_absorbed, mla_decode
-from tests._metrics import row_rel_err, tol_for
+from tests._metrics import record, row_rel_err, tol_for
 
 pytestmark = pytest.mark.gpu
 
@@ -57,9 +59,51 @@ def check_all_stages(inp, out, tol=None):
     assert np.array_equal(fin, np.isfinite(out["lse"])), "lse -inf pattern differs"
     errs["lse"] = float(np.max(np.abs(out["lse"][fin] - ref["lse"][fin]))) if fin.any() else 0.0
     print(c.name, {k: f"{v:.2e}" for k, v in errs.items()}, "splits", out["num_splits"], flush=True)
+    record(_label(c, out), errs, tol)
     for k, v in errs.items():
         assert v <= tol, (k, v, tol)
     return errs
+
+
+def _label(cfg, out):
+    t = os.environ.get("PYTEST_CURRENT_TEST", cfg.name).split(" ")[0].split("::")[-1]
+    return f"{t} [{cfg.name}, splits {out['num_splits']}]"
+
+
+def check_rows(inp, out, rows, tol=None, label=None):
+    """Stage-by-stage comparison on the (b, i, h) rows given (the oracle's
+    cost grows with the rows it computes; large cases sample them)."""
+    c = inp.cfg
+    tol = tol or tol_for(c)
+    idx = tuple(np.array(rows).T)
+    ab = mla_absorbed(inp, rows=rows)
+    ref = mla_decode(inp, rows=rows)
+    fin = np.isfinite(ref["lse"][idx])
+    assert np.array_equal(fin, np.isfinite(out["lse"][idx])), "lse -inf pattern differs"
+    errs = {
+        "q_lat": row_rel_err(out["q_abs"][..., :c.d_latent][idx], ab["q_lat"][idx]),
+        "q_pe": row_rel_err(out["q_abs"][..., c.d_latent:][idx], ab["q_pe"][idx]),
+        "o_lat": row_rel_err(out["o_lat"][idx], ab["o_lat"][idx]),
+        "o": row_rel_err(out["o"][idx], ref["o"][idx]),
+        "lse": float(np.max(np.abs(out["lse"][idx][fin] - ref["lse"][idx][fin]))) if fin.any() else 0.0,
+    }
+    label = label or _label(c, out)
+    print(f"{label}: {len(rows)} rows", {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
+    record(f"{label} ({len(rows)} rows)", errs, tol)
+    for k, v in errs.items():
+        assert v <= tol, (k, v, tol)
+    return errs
+
+
+def spread_rows(inp, n_heads=3, full_seqs=2):
+    """Every query of a few heads (first, last and one between) of every
+    sequence, plus all heads of the longest and of a middle sequence."""
+    c = inp.cfg
+    heads = sorted({0, c.heads - 1, *np.linspace(0, c.heads - 1, n_heads).astype(int).tolist()})
+    rows = {(b, i, h) for b in range(c.batch) for i in range(c.q_len) for h in heads}
+    for b in sorted({int(np.argmax(inp.seq_lens)), c.batch // 2})[:full_seqs]:
+        rows |= {(b, i, h) for i in range(c.q_len) for h in range(c.heads)}
+    return sorted(rows)
 
 
 # ---------------------------------------------------------------- fp32
@@ -206,6 +250,35 @@ def test_bf16_mfma_32_heads_and_empty_sequence():
         assert row_rel_err(out["o"][b], ref["o"][b]) < 2e-2
 
 
+# Batches of more than 64 sequences take the decode kernels' general setup
+# (tile totals summed over lane chunks, the unit's first sequence found by a
+# scan, the descriptor window built chunk by chunk).  Short ragged sequences
+# keep the oracle cheap; one split makes a unit walk all ~780 tiles and 7
+# splits ~110, so the 64-tile window slides many times.
+@pytest.mark.parametrize("splits", [None, 7, 1])
+@pytest.mark.parametrize("q_len", [1, 2])
+def test_bf16_batch_over_64(splits, q_len):
+    cfg = scaled(BF16_RAGGED, batch=130, paged=True, q_len=q_len, causal=q_len > 1,
+                 query_in_cache=q_len > 1, len_lo=max(1, q_len), len_hi=700, seed=4242 + q_len)
+    inp = MLAInputs(cfg)
+    inp.seq_lens[5] = q_len      # a sequence holding only its queries
+    inp.positions[5] = np.arange(q_len) if q_len > 1 else [q_len]
+    out = run_gpu(inp, num_splits=splits)
+    check_rows(inp, out, spread_rows(inp))
+
+
+# Batches of at most 64 whose units span more than 64 tiles: the descriptor
+# window slides inside the unit (one split over two ~5000-token sequences).
+@pytest.mark.parametrize("paged", [False, True])
+@pytest.mark.parametrize("splits", [1, 2])
+def test_bf16_long_unit_window_slides(paged, splits):
+    cfg = scaled(BF16_RAGGED, batch=2, paged=paged, len_lo=4700, len_hi=5200, seed=515)
+    inp = MLAInputs(cfg)
+    out = run_gpu(inp, num_splits=splits)
+    rows = [(b, 0, h) for b in range(2) for h in (0, 5, 64, 127)]
+    check_rows(inp, out, rows)
+
+
 # ------------------------------------------------ fused combine + W_UV
 
 # batch 130 / 70: 130 and 140 query rows, where the fused kernel takes 64 rows
@@ -220,7 +293,6 @@ def test_combine_out_proj_matches_two_calls(q_len, causal, batch):
     c = cfg
     d = mla.dims(c.batch, c.q_len, c.heads, c.d_nope, c.d_rope, c.d_latent, c.d_v,
                  DT[c.q_dtype], DT[c.kv_dtype])
-    run_gpu(inp, num_splits=9, dev=dev)  # fills nothing we keep; warms the path
     step = mla.DecodeStep(d, num_splits=9)
     step.run(q_nope=dev.q_nope, q_rope=dev.q_rope, positions=dev.positions, w_uk=dev.w_uk,
              w_uv=dev.w_uv, latent=dev.latent, rope=dev.rope, kv_row_stride=dev.kv_row_stride,
@@ -243,3 +315,12 @@ def test_combine_out_proj_matches_two_calls(q_len, causal, batch):
     assert row_rel_err(_np(o_lat_fused), _np(o_lat3)) < 1e-2
     assert row_rel_err(_np(o_fused), _np(o3)) < 1e-2
     assert float(torch.max(torch.abs(lse_fused - lse3))) < 1e-5
+    # the two separate calls (mla_combine, then mla_out_proj's MFMA kernel)
+    # and the fused call, each against the oracle on sampled rows
+    q_abs = _np(step.q_abs)
+    rows = spread_rows(inp)
+    sep = {"q_abs": q_abs, "o_lat": _np(o_lat3), "lse": _np(lse3), "o": _np(o3), "num_splits": 9}
+    check_rows(inp, sep, rows, label=f"two calls q_len {q_len} batch {batch}")
+    fus = {"q_abs": q_abs, "o_lat": _np(o_lat_fused), "lse": _np(lse_fused), "o": _np(o_fused),
+           "num_splits": 9}
+    check_rows(inp, fus, rows, label=f"fused call q_len {q_len} batch {batch}")
