@@ -78,7 +78,7 @@ typedef struct mla_dims {
   int32_t d_latent; /* latent width d_c (512)                                */
   int32_t d_v;      /* per-head value width (128)                            */
   int32_t q_dtype;  /* MLA_F32 or MLA_BF16: q_nope, q_rope, w_uk, w_uv,
-                       q_abs, o_lat, o                                       */
+                       o_lat, o (q_abs: fp32, or IEEE fp16 for MLA_BF16)     */
   int32_t kv_dtype; /* MLA_F32 (with q F32), MLA_BF16 or MLA_FP8_E4M3
                        (with q BF16): the cache                              */
   int32_t flags;    /* MLA_FLAG_* */
@@ -99,9 +99,14 @@ typedef struct mla_dims {
  *   positions [B, Lq]                     int32, token position of each query
  *   rope_base                             e.g. 10000
  *   w_uk      [H, d_nope, d_latent]       q_dtype, W_UK,i = w_uk[i] (d_nope x d_latent)
- *   q_abs     [B, Lq, H, d_latent+d_rope] q_dtype, output:
+ *   q_abs     [B, Lq, H, d_latent+d_rope] output, fp32 when q_dtype is
+ *             MLA_F32 and IEEE fp16 when it is MLA_BF16:
  *             q_abs[..., :d_latent] = w_uk[h]^T q_nope   (fp32 accumulate)
  *             q_abs[..., d_latent:] = RoPE(q_rope, pos)  (angle in fp64)
+ *             The fp16 form keeps 11 significant bits, so the scores of
+ *             long contexts with large cached values stay within the bf16
+ *             tolerance (a bf16 query moves them by ~1e-2); magnitudes
+ *             beyond 65504 saturate.
  */
 int mla_absorb_q(const mla_dims_t* dims, const void* q_nope, const void* q_rope,
                  const int32_t* positions, float rope_base, const void* w_uk,
@@ -124,7 +129,12 @@ int mla_absorb_q(const mla_dims_t* dims, const void* q_nope, const void* q_rope,
  * rope_cache = latent_cache + d_latent.  For MLA_FP8_E4M3 the stored value
  * is code * kv_scale[r] (one fp32 scale per token).
  *
- *   q_abs        [B, Lq, H, d_latent+d_rope] q_dtype (output of mla_absorb_q)
+ *   q_abs        [B, Lq, H, d_latent+d_rope] fp32 or fp16 (output of
+ *                mla_absorb_q).  bf16 cache rows are scored and summed in
+ *                fp16: every bf16 value of magnitude 2^-17 .. 65504 is an
+ *                fp16 value, so the conversion is exact there; larger
+ *                magnitudes saturate, smaller ones keep 2^-24 absolute
+ *                precision.
  *   seq_lens     [B] int32, cached tokens per sequence
  *   block_table  [B, max_blocks_per_seq] int32, or NULL for contiguous rows
  *   block_size   must be MLA_TILE_TOKENS when block_table != NULL
@@ -211,9 +221,8 @@ int mla_workspace_elems(const mla_dims_t* dims, int32_t num_splits, int64_t* o_p
 int mla_workspace_bytes(const mla_dims_t* dims, int32_t num_splits, int64_t* o_part_bytes,
                         int64_t* lse_part_bytes);
 
-/* A good num_splits for `device`: one work unit per compute unit and row
- * group (64 query rows when queries and cache are bf16, 128 otherwise).
- * Host-only query of device properties. */
+/* A good num_splits for `device`: one work unit per compute unit and
+ * block of 128 query rows.  Host-only query of device properties. */
 int mla_num_splits_hint(const mla_dims_t* dims, int32_t device, int32_t* num_splits);
 
 /*

@@ -43,6 +43,17 @@ __host__ __device__ inline float e4m3_to_f32(uint8_t c) {
   return (c & 0x80) ? -v : v;
 }
 
+// IEEE binary16 with saturation: finite values beyond +-65504 become
+// +-65504 (the absorbed query is carried in fp16; its 11-bit significand
+// keeps the scores of long, outlier-heavy contexts accurate, and the clamp
+// keeps an out-of-range query finite instead of turning scores into NaN).
+__device__ inline _Float16 f32_to_f16_sat(float f) {
+  return (_Float16)fminf(fmaxf(f, -65504.f), 65504.f);
+}
+__device__ inline uint16_t f32_to_f16_sat_bits(float f) {
+  return __builtin_bit_cast(uint16_t, f32_to_f16_sat(f));
+}
+
 template <typename T> struct Elem;
 template <> struct Elem<float> {
   __device__ static float load(const float* p, int64_t i) { return p[i]; }
@@ -51,6 +62,10 @@ template <> struct Elem<float> {
 template <> struct Elem<uint16_t> {  // bf16 bits
   __device__ static float load(const uint16_t* p, int64_t i) { return bf16_to_f32(p[i]); }
   __device__ static void store(uint16_t* p, int64_t i, float v) { p[i] = f32_to_bf16(v); }
+};
+template <> struct Elem<_Float16> {
+  __device__ static float load(const _Float16* p, int64_t i) { return (float)p[i]; }
+  __device__ static void store(_Float16* p, int64_t i, float v) { p[i] = f32_to_f16_sat(v); }
 };
 template <> struct Elem<uint8_t> {  // e4m3 codes
   __device__ static float load(const uint8_t* p, int64_t i) { return e4m3_to_f32(p[i]); }

@@ -6,43 +6,33 @@
 //
 // Query rows are (query i, head h) pairs, row i*H + h.  The cache is walked
 // in 32-token sub-tiles, each staged once in LDS for all the workgroup's rows
-// ([ARCH] 3.1: every head scores the same raw latent).
+// ([ARCH] 3.1: every head scores the same raw latent).  Both kernels compute
+// in fp16: the absorbed query arrives in fp16, and the staged cache rows are
+// converted exactly to fp16 in LDS (every bf16 value of magnitude 2^-17 ..
+// 65504 and every e4m3 value is an fp16 value), so scores against long
+// contexts with large cached values keep the query's 11-bit significand.
 //
-// decode_hs_kernel (bf16 cache): one workgroup = one split-K unit x 64 rows,
-// 8 waves with fixed roles, the two roles working on consecutive sub-tiles:
-//
-//   scores   waves 0-3, wave v owns rows 16v..16v+15: S^T = K Q^T with
-//            v_mfma_f32_16x16x32_bf16 (K = tile rows from LDS as A, the
-//            wave's 18 k-slices of absorbed query in registers as B);
-//            online softmax in log2 units with a lazy rescale; P (bf16) to
-//            one of two LDS buffers.
-//   values   waves 4-7, wave c owns latent columns 128c..128c+127 of all 64
-//            rows: O[:, cols] += P V[:, cols] with v_mfma_f32_32x32x16_bf16
-//            (P from LDS as A, V = the tile's latent part read transposed
-//            with ds_read_b64_tr_b16 as B); they also issue the direct loads.
+// decode_sf_kernel (bf16 cache): one workgroup = one split-K unit x 128 rows,
+// 8 waves, each owning 16 rows for both products (see the kernel).
 //
 // decode_fp8_kernel (fp8 e4m3 cache with per-token scales): one workgroup =
 // one split-K unit x 128 rows, every wave in both roles in turn (wave w
 // scores rows 16w.. with 11 k-slices in registers and 7 in LDS, then sums
 // latent columns 64w.. for all 128 rows); each staged sub-tile is first
-// converted exactly to bf16 in LDS, and the scales enter the scores and P.
+// converted exactly to fp16 in LDS, and the scales enter the scores and P.
 //
 // Operand layouts:
 //   16x16x32  A: lane l row l%16, k 8(l/16)..+7; B: column l%16, same k;
 //             C: column l%16, rows 4(l/16)..+3
 //   32x32x16  A: lane l row l%32, k 8(l/32)..+7; B: column l%32, same k;
 //             C: column l%32, rows 8(r/4) + 4(l/32) + r%4, r = 0..15
-// The order of k inside one MFMA is immaterial when A and B agree; P is
-// stored so that each lane's 16-byte A operand holds tokens
-// {16ks + 4hf + 0..3, 16ks + 8 + 4hf + 0..3}, the rows its two transposed V
-// reads return.
+// The order of k inside one MFMA is immaterial when A and B agree.
 //
 // Sub-tile LDS layout (32 rows x 72 16-byte chunks = 36 KB): 1 KB blocks of
 // 8 rows x 8 chunks, block (cg, rg) at (cg*4 + rg) KB; inside, row rho /
 // chunk kappa at entry 8*(kappa ^ (rg&1)) + (rho ^ 4*((kappa ^ kappa>>1)&1)),
 // which keeps the score reads and the transposed value reads free of bank
-// conflicts.  Each block is one wave-wide direct global->LDS load.  Rings of
-// 4 (bf16) and 3 (fp8 staging) sub-tiles keep two loads in flight.
+// conflicts.  Each block is one wave-wide direct global->LDS load.
 //
 // The loop is latency-bound before it is bandwidth-bound, so it avoids
 // anything that stalls a wave on memory: the unit's tile descriptors
@@ -183,9 +173,9 @@ __device__ __forceinline__ void issue_all_f8(const F8Plan& p, int w) {
   }
 }
 
-// Exact e4m3 -> bf16 conversion of a staged sub-tile into the bf16 tile
-// layout (every e4m3 value is a bf16 value, so the unit-scale hardware
-// conversion is exact).  512 threads, 2304 chunks of 8: thread t takes chunks
+// Exact e4m3 -> fp16 conversion of a staged sub-tile into the tile layout
+// (every e4m3 value is an fp16 value, so the unit-scale hardware conversion
+// is exact).  512 threads, 2304 chunks of 8: thread t takes chunks
 // t + 512 i, i.e. row r0 + 7 i (+1 when the chunk index wraps) of 72 chunks.
 __device__ __forceinline__ void convert_f8(const char* stage, char* tile, int tid) {
   int r = tid / 72, kap = tid - 72 * (tid / 72);
@@ -194,14 +184,14 @@ __device__ __forceinline__ void convert_f8(const char* stage, char* tile, int ti
     if (i < 4 || tid < 2304 - 4 * 512) {
       const uint2 raw = *(const uint2*)(stage + (kap < 64 ? r * 512 + kap * 8
                                                           : 16384 + r * 64 + (kap - 64) * 8));
-      const bf16x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)raw.x, 1.0f, false);
-      const bf16x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)raw.x, 1.0f, true);
-      const bf16x2 v2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)raw.y, 1.0f, false);
-      const bf16x2 v3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)raw.y, 1.0f, true);
-      const bf16x8 v = {v0.x, v0.y, v1.x, v1.y, v2.x, v2.y, v3.x, v3.y};
+      const f16x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)raw.x, 1.0f, false);
+      const f16x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)raw.x, 1.0f, true);
+      const f16x2 v2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)raw.y, 1.0f, false);
+      const f16x2 v3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)raw.y, 1.0f, true);
+      const f16x8 v = {v0.x, v0.y, v1.x, v1.y, v2.x, v2.y, v3.x, v3.y};
       const int cg = kap >> 3, kc = kap & 7, rg = r >> 3, rho = r & 7;
       const int entry = 8 * (kc ^ (rg & 1)) + (rho ^ (4 * ((kc ^ (kc >> 1)) & 1)));
-      *(bf16x8*)(tile + (cg * 4 + rg) * 1024 + entry * 16) = v;
+      *(f16x8*)(tile + (cg * 4 + rg) * 1024 + entry * 16) = v;
     }
     // next chunk: + 512 = 7 rows + 8 chunks
     r += 7;
@@ -306,7 +296,7 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(DecodeArgs a) {
   step_sub(px, phh);
 
   constexpr int kQReg = L::kQReg;
-  bf16x8 q[kQReg];
+  f16x8 q[kQReg];
   f32x16 o[4][2];
   float m_run = -INFINITY, l_run = 0.f;
   bool new_seg = true;
@@ -318,13 +308,13 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(DecodeArgs a) {
     if (new_seg) {
       new_seg = false;
       {  // unconditional (inactive waves read row 0) so q is dead between segments
-        const bf16x8* qp = (const bf16x8*)((const uint16_t*)a.q_abs +
+        const f16x8* qp = (const f16x8*)((const _Float16*)a.q_abs +
                                             (((int64_t)ci.b * a.q_len + qi) * a.heads + h0 + li) * 576);
 #pragma unroll
         for (int kk = 0; kk < kQReg; ++kk) q[kk] = qp[4 * kk + g];
 #pragma unroll
         for (int kk = kQReg; kk < 18; ++kk)
-          *(bf16x8*)(smem + off_ql(ln, w) + (kk - kQReg) * 8192) = qp[4 * kk + g];
+          *(f16x8*)(smem + off_ql(ln, w) + (kk - kQReg) * 8192) = qp[4 * kk + g];
       }
       wait_vm0();
 #pragma unroll
@@ -365,7 +355,7 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(DecodeArgs a) {
     const bool scores = has_tokens && qk_active && nv > 0;  // uniform per wave
     if (has_tokens) {
       // ---------------- scores and softmax for this wave's 16 rows
-      bf16x8 pw = bf16x8{};
+      f16x8 pw = f16x8{};
       bool need = false;
       float alpha = 1.f;
       if (scores) {
@@ -373,13 +363,13 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(DecodeArgs a) {
         constexpr int kPf = 2;
         const int lq = fresh_lane();
         const uint32_t o_qk = off_qk(lq), o_ql = off_ql(lq, w);
-        bf16x8 ka[kPf + 1][2], qb[kPf + 1];
+        f16x8 ka[kPf + 1][2], qb[kPf + 1];
         auto kload = [&](int kk) {
           const int e = kk % (kPf + 1);
 #pragma unroll
           for (int j = 0; j < 2; ++j)
-            ka[e][j] = *(const bf16x8*)(tile + (uint32_t)((kk >> 1) * 4096 + 2048 * j + 512 * (kk & 1)) + o_qk);
-          if (kk >= kQReg) qb[e] = *(const bf16x8*)(smem + o_ql + (kk - kQReg) * 8192);
+            ka[e][j] = *(const f16x8*)(tile + (uint32_t)((kk >> 1) * 4096 + 2048 * j + 512 * (kk & 1)) + o_qk);
+          if (kk >= kQReg) qb[e] = *(const f16x8*)(smem + o_ql + (kk - kQReg) * 8192);
         };
 #pragma unroll
         for (int kk = 0; kk < kPf; ++kk) kload(kk);
@@ -387,9 +377,9 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(DecodeArgs a) {
         for (int kk = 0; kk < 18; ++kk) {
           if (kk + kPf < 18) kload(kk + kPf);
           const int e = kk % (kPf + 1);
-          const bf16x8 qk = kk < kQReg ? q[kk < kQReg ? kk : 0] : qb[e];
-          s[0] = mfma16(ka[e][0], qk, s[0]);
-          s[1] = mfma16(ka[e][1], qk, s[1]);
+          const f16x8 qk = kk < kQReg ? q[kk < kQReg ? kk : 0] : qb[e];
+          s[0] = mfma16h(ka[e][0], qk, s[0]);
+          s[1] = mfma16h(ka[e][1], qk, s[1]);
           __builtin_amdgcn_sched_barrier(0);
         }
         mfma_settle(s[0]);
@@ -431,14 +421,14 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(DecodeArgs a) {
             const float e = __builtin_amdgcn_exp2f(fmaf(s[j][r], sl2, -m_use));
             l_run += e;
             // fp8: the value rows in LDS are unscaled, so P carries the scale
-            pw[4 * j + r] = (__bf16)(e * sc[j][r]);
+            pw[4 * j + r] = (_Float16)(e * sc[j][r]);
           }
       }
       // P rows of this wave's heads (zeros when it has nothing to score)
       {
         const uint32_t o_pw = off_pw(fresh_lane(), w);
-        *(bf16x4*)(pb + o_pw) = __builtin_shufflevector(pw, pw, 0, 1, 2, 3);
-        *(bf16x4*)(pb + o_pw + 32) = __builtin_shufflevector(pw, pw, 4, 5, 6, 7);
+        *(f16x4*)(pb + o_pw) = __builtin_shufflevector(pw, pw, 0, 1, 2, 3);
+        *(f16x4*)(pb + o_pw + 32) = __builtin_shufflevector(pw, pw, 4, 5, 6, 7);
       }
       // every wave publishes its factors (1 when unchanged): a rescale reads all rows
       if ((ln >> 4) == 0) alpha_buf[16 * w + (ln & 15)] = alpha;
@@ -466,19 +456,19 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(DecodeArgs a) {
       const uint32_t o_pr = off_pr(lv), o_pv0 = off_pv(lv, w, 0), o_pv1 = off_pv(lv, w, 1);
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        bf16x8 pa[4], vb[2];
+        f16x8 pa[4], vb[2];
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb)
-          pa[mb] = *(const bf16x8*)(pb + o_pr + (uint32_t)(mb * 32 * kPPitch + ks * 32));
+          pa[mb] = *(const f16x8*)(pb + o_pr + (uint32_t)(mb * 32 * kPPitch + ks * 32));
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) {
           const uint32_t cb = (uint32_t)(2048 * ks + 512 * nb);
-          vb[nb] = cat(lds_tr4(tile, cb + o_pv0), lds_tr4(tile, cb + o_pv1));
+          vb[nb] = cath(lds_tr4h(tile, cb + o_pv0), lds_tr4h(tile, cb + o_pv1));
         }
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-          for (int nb = 0; nb < 2; ++nb) o[mb][nb] = mfma32(pa[mb], vb[nb], o[mb][nb]);
+          for (int nb = 0; nb < 2; ++nb) o[mb][nb] = mfma32h(pa[mb], vb[nb], o[mb][nb]);
       }
     }
 
@@ -528,41 +518,35 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(DecodeArgs a) {
 
 
 // ---------------------------------------------------------------------------
-// bf16 cache, head-split kernel with specialised waves.  A workgroup takes
-// 64 of the query rows (two workgroups per 128: the second one, 128 units
-// later in launch order, runs on the same XCD and finds the tiles its sibling
-// just read in L2).  Waves 0-3 only score: wave v holds all 18 k-slices of
-// its 16 rows' absorbed query in registers and runs the online softmax;
-// waves 4-7 only sum values (wave c: the 64 rows x latent columns
-// 128c..128c+127) and issue the direct loads.  The roles overlap in time:
+// bf16 cache, single-fill kernel.  One workgroup per split-K unit holds a
+// block of 128 query rows, so every 32-token sub-tile is loaded into LDS
+// once for all of them ([ARCH] 3.1: every head scores the same raw latent).
+// Each of the 8 waves owns 16 rows for the whole walk:
 //
-//   phase k   score waves: S, P of sub-tile k      value waves: P V of k-1,
-//                                                  loads of sub-tile k+2
+//   scores  S^T = K Q^T on v_mfma_f32_16x16x32_f16 (K from LDS as A, the
+//           wave's 18 k-slices of fp16 query in registers as B); lane l
+//           holds row l%16 and tokens 4(l/16)..+3 of each 16-token block;
+//           online softmax in log2 units with a lazy rescale;
+//   values  O^T += V^T P^T on the same instruction: V^T (16 latent columns
+//           x 32 tokens) read transposed from LDS with ds_read_b64_tr_b16 as
+//           A, and P^T straight from the score registers as B (the k order
+//           of one MFMA only has to agree between A and B: lane l supplies
+//           tokens {4(l/16)..+3, 16+4(l/16)..+3}, the two transposed reads
+//           return the same tokens).  Lane l accumulates row l%16, so the
+//           rescale factor and 1/l are per-lane scalars.
 //
-// with P, the rescale factors and the row totals double-buffered by sub-tile
-// parity and a ring of four sub-tiles (k+2 loading, k+1 landed, k scored,
-// k-1 summed).  Each role runs its own loop over the nsub + 1 phases with one
-// barrier per phase, so a wave only keeps its own role's state live.
-constexpr int kHsRows = 64;
-constexpr int kHsRing = 4;
-struct LdsHS {
-  static constexpr int kPBuf = kHsRows * kPPitch;       // 5120
-  static constexpr int kOffP = kHsRing * kSubBytes;     // 147456: two P buffers
-  static constexpr int kOffAlpha = kOffP + 2 * kPBuf;   // 2 x 64 floats
-  static constexpr int kOffInvL = kOffAlpha + 512;      // 2 x 64 floats: 1/l or 0
-  static constexpr int kOffLse = kOffInvL + 512;        // 2 x 64 floats
-  static constexpr int kOffFlag = kOffLse + 512;        // 2 x 4 bytes
-  static constexpr int kBytes = kOffFlag + 64;          // 159296
-};
-static_assert(LdsHS::kBytes <= 163840, "LDS budget");
-
-// All nine direct loads of row group (w & 3) of a sub-tile (value waves).
-__device__ __forceinline__ void issue_rows(const DmaPlan& p, int w) {
-  const uint32_t m0 = p.dst + (uint32_t)((w & 3) * 1024);
-#pragma unroll
-  for (int cg = 0; cg < 8; ++cg) lds_dma16_stream(p.lat, p.voff + cg * 128, m0 + cg * 4096);
-  lds_dma16_stream(p.rop, p.voff, m0 + 8 * 4096);
-}
+// Waves never exchange data; they meet at one barrier per sub-tile, after
+// which the next sub-tile is complete in LDS and the oldest ring slot is
+// free.  In the value part of sub-tile s each wave issues its share of the
+// direct loads of sub-tile s+3 (row group w&3; column groups 0-4 for waves
+// 0-3, 5-8 for waves 4-7) and converts, bf16 -> fp16 in place, the chunks
+// it loaded of sub-tile s+1 after waiting for them itself.
+constexpr int kSfRows = 128;
+constexpr int kSfRing = 4;
+constexpr int kSfSplit = 5;      // column groups [0, 5) loaded by waves 0-3, [5, 9) by waves 4-7
+constexpr int kSfKPrefetch = 2;  // K operands read ahead of the score MFMAs
+constexpr int kSfBytes = kSfRing * kSubBytes;  // 147456
+static_assert(kSfBytes <= 163840, "LDS budget");
 
 // Load cg (0-7 latent, 8 RoPE) of row group (w & 3).
 __device__ __forceinline__ void issue_cg(const DmaPlan& p, int w, int cg) {
@@ -573,14 +557,38 @@ __device__ __forceinline__ void issue_cg(const DmaPlan& p, int w, int cg) {
     lds_dma16_stream(p.rop, p.voff, m0);
 }
 
-__global__ __launch_bounds__(512, 1) void decode_hs_kernel(DecodeArgs a) {
-  using L = LdsHS;
-  __shared__ __attribute__((aligned(1024))) char smem[L::kBytes];
+// Two bf16 values -> fp16 (exact for magnitudes 2^-17 .. 65504; the
+// round-toward-zero conversion saturates larger ones at 65504).
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t d) {
+  typedef __fp16 fp16x2_t __attribute__((ext_vector_type(2)));
+  const fp16x2_t h = __builtin_amdgcn_cvt_pkrtz(__uint_as_float(d << 16), __uint_as_float(d & 0xffff0000u));
+  return __builtin_bit_cast(uint32_t, h);
+}
+__device__ __forceinline__ uint4 bf16x8_to_f16x8(uint4 c) {
+  return make_uint4(bf16x2_to_f16x2(c.x), bf16x2_to_f16x2(c.y), bf16x2_to_f16x2(c.z),
+                    bf16x2_to_f16x2(c.w));
+}
+
+// Lane part of the V^T operand address (16x16x32 A: lane l holds latent
+// column 16 nb + l%16, tokens 4(l/16)..+3 for rd = 0, 16 + 4(l/16)..+3 for
+// rd = 1).  Lane l names token 16 rd + 4g + i/4 and columns
+// 16 nb + 4(i%4)..+3 (g = l/16, i = l%16); in the sub-tile layout that
+// address is this base (which depends on nb only through its parity) plus
+// (nb/4) * 4096 + (nb%4) * 256.  The reads are free of bank conflicts.
+__device__ __forceinline__ uint32_t vt_base(int lane, int rd, int par) {
+  const int g = lane >> 4, i = lane & 15;
+  const int rg = 2 * rd + (g >> 1);
+  const int rho = 4 * (g & 1) + (i >> 2);
+  const int b = (i >> 1) & 1;
+  return (uint32_t)(rg * 1024 + 128 * (b ^ (rg & 1)) + 16 * (rho ^ (4 * ((b ^ par) & 1))) + 8 * (i & 1));
+}
+
+__global__ __launch_bounds__(512, 1) void decode_sf_kernel(DecodeArgs a) {
+  __shared__ __attribute__((aligned(1024))) char smem[kSfBytes];
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int R = a.q_len * a.heads;
-  const int rowb = blockIdx.y * kHsRows;  // first query row of this workgroup
   const int u = blockIdx.x;
 
   int64_t x0, x1;  // this unit's tiles
@@ -601,259 +609,205 @@ __global__ __launch_bounds__(512, 1) void decode_hs_kernel(DecodeArgs a) {
   }
 
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_char*)smem;
-  float* alpha_buf = (float*)(smem + L::kOffAlpha);
-  float* invl_buf = (float*)(smem + L::kOffInvL);
-  float* lse_buf = (float*)(smem + L::kOffLse);
-  uint8_t* flags = (uint8_t*)(smem + L::kOffFlag);
   const int64_t nsub = 2 * (x1 - x0);  // a unit has >= 1 tile = 2 sub-tiles
-  int64_t cx = x0;  // tile of this wave's current sub-tile
-  int chh = 0;      // and its half
+  const int cg0 = w < 4 ? 0 : kSfSplit, cg1 = w < 4 ? kSfSplit : 9;
+  const int n_share = cg1 - cg0;  // direct loads per sub-tile of this wave
 
-  if (w >= 4) {
-    // ======================= value waves: loads, then O[:, 128c..] += P V
-    const int c = w - 4;
-    int64_t px = x0;  // next sub-tile to load
-    int phh = 0;
-    issue_rows(plan_sub(a, tile_info(win, px), phh, lds0, w, lane), w);
+  // rows of this wave
+  const int qrow0 = blockIdx.y * kSfRows + 16 * w;
+  const bool active = qrow0 < R;  // uniform per wave
+  const int qi = active ? qrow0 / a.heads : 0;
+  const int h0 = active ? qrow0 % a.heads : 0;
+  const float sl2 = a.softmax_scale * kLog2e;
+
+  // next sub-tile to load: tile px, half phh, ring index pz
+  int64_t px = x0, pz = 0;
+  int phh = 0;
+  auto plan_next = [&](int ln) {
+    if (px >= win.wx + win.wn)  // slide the window to start at the tile in use
+      build_window(a, px - 2, x1, win.b0, win.pb0, ln, win);
+    const DmaPlan plan = plan_sub(a, tile_info(win, px), phh, lds0 + (uint32_t)((pz & 3) * kSubBytes), w, ln);
     step_sub(px, phh);
-    issue_rows(plan_sub(a, tile_info(win, px), phh, lds0 + (uint32_t)kSubBytes, w, lane), w);
-    step_sub(px, phh);
-    wait_vm(9);
-    block_sync();  // sub-tile 0 in LDS
+    ++pz;
+    return plan;
+  };
+  // this wave's loaded chunks of sub-tile z, bf16 -> fp16 in place, once
+  // they have landed (its loads of later sub-tiles may stay in flight)
+  auto convert_sub = [&](int64_t z, int ln) {
+    wait_vm((int)(n_share * (pz - 1 - z)));
+    char* base = smem + (int)(z & 3) * kSubBytes + (w & 3) * 1024 + 16 * ln;
+    uint4 c[kSfSplit];
+#pragma unroll
+    for (int i = 0; i < kSfSplit; ++i)
+      if (i < n_share) c[i] = *(const uint4*)(base + (cg0 + i) * 4096);
+#pragma unroll
+    for (int i = 0; i < kSfSplit; ++i)
+      if (i < n_share) *(uint4*)(base + (cg0 + i) * 4096) = bf16x8_to_f16x8(c[i]);
+  };
 
-    f32x16 o[2][4];
+  f16x8 q[18];
+  auto load_q = [&](int b, int ln) {
+    // unconditional (inactive waves read row 0) so q is dead between segments
+    const int li = ln & 15, gq = ln >> 4;
+    const f16x8* qp = (const f16x8*)((const _Float16*)a.q_abs +
+                                     (((int64_t)b * a.q_len + qi) * a.heads + h0 + li) * 576);
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb) o[mb][nb] = f32x16{};
+    for (int kk = 0; kk < 18; ++kk) q[kk] = qp[4 * kk + gq];
+  };
 
-    for (int64_t k = 0; k <= nsub; ++k) {
-      // the loads of sub-tile k+2, into the slot sub-tile k-2 used, go out
-      // between the value MFMAs so that their issue stalls overlap them
-      const bool more = k + 2 < nsub;
-      DmaPlan plan{};
-      int issued = more ? 0 : 9;
-      if (more) {
-        const int ln = fresh_lane();
-        if (px >= win.wx + win.wn)  // slide the window to start at the tile in use
-          build_window(a, cx, x1, win.b0, win.pb0, ln, win);
-        plan = plan_sub(a, tile_info(win, px), phh, lds0 + (uint32_t)(((k + 2) & 3) * kSubBytes),
-                        w, ln);
-        step_sub(px, phh);
-      }
-      if (k >= 1) {  // sub-tile j = k-1, scored in the previous phase
-        const int64_t j = k - 1;
-        const int jb = (int)(j & 1);
-        const TileInfo ci = tile_info(win, cx);
-        const char* tile = smem + (int)(j & 3) * kSubBytes;
-        const char* pb = smem + L::kOffP + jb * L::kPBuf;
-        if (32 * chh < ci.rem) {
-          const uint32_t fl = *(const uint32_t*)(flags + 4 * jb);
-          if (fl != 0) {  // rare: some row moved its reference max
-            const int lr = fresh_lane();
+  // ---- prologue: sub-tiles 0..2 in flight, this wave's query, sub-tile 0 converted
+  for (int z = 0; z < 3 && z < nsub; ++z) {
+    const DmaPlan plan = plan_next(lane);
+    for (int cg = cg0; cg < cg1; ++cg) issue_cg(plan, w, cg);
+  }
+  load_q(tile_info(win, x0).b, lane);
+  wait_vm0();
+  convert_sub(0, lane);
+  block_sync();
+
+  f32x4 o[32];  // O^T: column block nb holds latent columns 16 nb + 4(l/16)..+3 of row l%16
 #pragma unroll
-            for (int mb = 0; mb < 2; ++mb) {
-              f32x16 a16;
-#pragma unroll
-              for (int r4 = 0; r4 < 4; ++r4) {
-                const f32x4 a4 = *(const f32x4*)(alpha_buf + 64 * jb + mb * 32 + 8 * r4 + 4 * (lr >> 5));
-#pragma unroll
-                for (int i = 0; i < 4; ++i) a16[4 * r4 + i] = a4[i];
-              }
-#pragma unroll
-              for (int nb = 0; nb < 4; ++nb) o[mb][nb] *= a16;
-              __builtin_amdgcn_sched_barrier(0);
-            }
-          }
-          // the RoPE block's load first, the eight latent blocks' between the
-          // MFMAs (all nine at the top, or two per MFMA slot, measured slower)
-          if (more) issue_cg(plan, w, 8);
-          const int lv = fresh_lane();
-          const uint32_t o_pr = off_pr(lv);
-          const uint32_t o_pv0 = off_pv(lv, 2 * c, 0), o_pv1 = off_pv(lv, 2 * c, 1);
-#pragma unroll
-          for (int ks = 0; ks < 2; ++ks) {
-            bf16x8 pa[2], vb[4];
-#pragma unroll
-            for (int mb = 0; mb < 2; ++mb)
-              pa[mb] = *(const bf16x8*)(pb + o_pr + (uint32_t)(mb * 32 * kPPitch + ks * 32));
-#pragma unroll
-            for (int nb = 0; nb < 4; ++nb) {
-              const uint32_t cb = (uint32_t)(2048 * ks + 4096 * (nb >> 1) + 512 * (nb & 1));
-              vb[nb] = cat(lds_tr4(tile, cb + o_pv0), lds_tr4(tile, cb + o_pv1));
-            }
-#pragma unroll
-            for (int nb = 0; nb < 4; ++nb) {
-              if (more) issue_cg(plan, w, 4 * ks + nb);
-#pragma unroll
-              for (int mb = 0; mb < 2; ++mb) o[mb][nb] = mfma32(pa[mb], vb[nb], o[mb][nb]);
-              __builtin_amdgcn_sched_barrier(0);
-            }
-          }
-          issued = 9;
-        }
-        const bool last = j + 1 >= nsub || (chh == 1 && ci.rem <= kTile);
-        if (last) {  // end of this unit's part of the sequence: write the partial
-          const int64_t sl = (int64_t)u + ci.b;
-          const int lw = fresh_lane();
-          if ((lw >> 4) == 0 && rowb + 16 * c + (lw & 15) < R)
-            a.lse_part[sl * R + rowb + 16 * c + (lw & 15)] = lse_buf[64 * jb + 16 * c + (lw & 15)];
-          // fp16 partial rows of 1 KB; rows past R fall outside the resource
-          // and are dropped
-          const int rows_here = min(kHsRows, R - rowb);
-          const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(
-              (_Float16*)a.o_part + (sl * R + rowb) * 512, (uint32_t)rows_here * 1024u);
-          const uint32_t vo = (uint32_t)((4 * (lw >> 5) * 512 + 128 * c + (lw & 31)) * 2);
-#pragma unroll
-          for (int mb = 0; mb < 2; ++mb) {
-            f32x16 inv16;
-#pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-              const f32x4 l4 = *(const f32x4*)(invl_buf + 64 * jb + mb * 32 + 8 * r4 + 4 * (lw >> 5));
-#pragma unroll
-              for (int i = 0; i < 4; ++i) inv16[4 * r4 + i] = l4[i];
-            }
-#pragma unroll
-            for (int nb = 0; nb < 4; ++nb) {
-              const f32x16 vv = o[mb][nb] * inv16;
-#pragma unroll
-              for (int r = 0; r < 16; ++r) {
-                const uint32_t so = (uint32_t)((mb * 32 + 8 * (r >> 2) + (r & 3)) * 1024);
-                buffer_store_f16(vv[r], rs, vo + 64 * nb, so);
-              }
-              o[mb][nb] = f32x16{};
-            }
-          }
-          wait_vm0();  // keeps the hand-counted load waits exact
-        }
-        step_sub(cx, chh);
-      }
-      for (int cg = issued; cg < 9; ++cg) issue_cg(plan, w, cg);  // the rest (all, without a value sum)
-      if (k + 1 < nsub) wait_vm(more ? 9 : 0);  // sub-tile k+1 landed
-      block_sync();
+  for (int nb = 0; nb < 32; ++nb) o[nb] = f32x4{};
+  float m_run = -INFINITY, l_run = 0.f;
+  bool new_seg = false;  // the first segment's query is loaded
+  int64_t cx = x0;       // tile of the current sub-tile
+  int chh = 0;           // and its half
+
+  for (int64_t s = 0; s < nsub; ++s) {
+    int ln = fresh_lane();
+    const TileInfo ci = tile_info(win, cx);
+    if (new_seg) {
+      new_seg = false;
+      load_q(ci.b, ln);
+      m_run = -INFINITY;
+      l_run = 0.f;
     }
-  } else {
-    // ======================= score waves: S = Q K^T, online softmax, P
-    // Each SIMD runs one score wave and one value wave; the next phase waits
-    // on this wave's P, so its instructions go first when both are ready.
-    __builtin_amdgcn_s_setprio(3);
-    const int qrow0 = rowb + 16 * w;  // rows this wave scores
-    const bool qk_active = qrow0 < R;
-    const int qi = qk_active ? qrow0 / a.heads : 0;
-    const int h0 = qk_active ? qrow0 % a.heads : 0;
-    const float sl2 = a.softmax_scale * kLog2e;
-    bf16x8 q[18];
-    float m_run = -INFINITY, l_run = 0.f;
-    bool new_seg = true;
-    block_sync();  // pairs with the value waves' first barrier
+    const char* tile = smem + (int)(s & 3) * kSubBytes;
+    // visible tokens of this sub-tile: all up to the sequence end, or with
+    // the causal mask those up to the query's own position
+    int nv = ci.rem - 32 * chh - (a.causal ? a.q_len - 1 - qi : 0);
+    nv = nv < 0 ? 0 : (nv > kSub ? kSub : nv);
+    const bool work = active && nv > 0;  // uniform per wave
+    const bool last = s + 1 >= nsub || (chh == 1 && ci.rem <= kTile);
+    const bool more = s + 3 < nsub;
+    DmaPlan plan{};
+    if (more) plan = plan_next(ln);
+    int issued = cg0;  // column groups of sub-tile s+3 issued so far
 
-    for (int64_t k = 0; k <= nsub; ++k) {
-      if (k < nsub) {
-        int ln = fresh_lane();
-        if (cx >= win.wx + win.wn) build_window(a, cx, x1, win.b0, win.pb0, ln, win);
-        const TileInfo ci = tile_info(win, cx);
-        if (new_seg) {
-          new_seg = false;
-          // unconditional (inactive waves read row 0) so q is dead between segments
-          const int li = ln & 15, g = ln >> 4;
-          const bf16x8* qp = (const bf16x8*)((const uint16_t*)a.q_abs +
-                                              (((int64_t)ci.b * a.q_len + qi) * a.heads + h0 + li) * 576);
+    if (work) {
+      // ------------------------------------------------ scores and softmax
+      f32x4 sc[2] = {f32x4{}, f32x4{}};  // token block jt: tokens 16 jt + 4(l/16)..+3
+      {
+        constexpr int kPf = kSfKPrefetch;
+        const uint32_t o_qk = off_qk(fresh_lane());
+        f16x8 ka[kPf + 1][2];
+        auto kload = [&](int kk) {
+          const int e = kk % (kPf + 1);
 #pragma unroll
-          for (int kk = 0; kk < 18; ++kk) q[kk] = qp[4 * kk + g];
-          m_run = -INFINITY;
-          l_run = 0.f;
+          for (int jt = 0; jt < 2; ++jt)
+            ka[e][jt] = *(const f16x8*)(tile + (uint32_t)((kk >> 1) * 4096 + 2048 * jt + 512 * (kk & 1)) + o_qk);
+        };
+#pragma unroll
+        for (int kk = 0; kk < kPf; ++kk) kload(kk);
+#pragma unroll
+        for (int kk = 0; kk < 18; ++kk) {
+          if (kk + kPf < 18) kload(kk + kPf);
+          const int e = kk % (kPf + 1);
+          sc[0] = mfma16h(ka[e][0], q[kk], sc[0]);
+          sc[1] = mfma16h(ka[e][1], q[kk], sc[1]);
+          __builtin_amdgcn_sched_barrier(0);
         }
-        const int kb = (int)(k & 1);
-        const char* tile = smem + (int)(k & 3) * kSubBytes;
-        const bool has_tokens = 32 * chh < ci.rem;  // uniform: an empty second half does nothing
-        int nv = ci.rem - 32 * chh - (a.causal ? a.q_len - 1 - qi : 0);
-        nv = nv < 0 ? 0 : (nv > kSub ? kSub : nv);
-        const bool scores = has_tokens && qk_active && nv > 0;  // uniform per wave
-        const bool last = k + 1 >= nsub || (chh == 1 && ci.rem <= kTile);
-        if (has_tokens) {
-          bf16x8 pw = bf16x8{};
-          bool need = false;
-          float alpha = 1.f;
-          if (scores) {
-            // token block j x k-slice parity: four accumulator chains
-            f32x4 s[2][2] = {{f32x4{}, f32x4{}}, {f32x4{}, f32x4{}}};
-            constexpr int kPf = 4;
-            const uint32_t o_qk = off_qk(fresh_lane());
-            bf16x8 ka[kPf + 1][2];
-            auto kload = [&](int kk) {
-              const int e = kk % (kPf + 1);
-#pragma unroll
-              for (int jt = 0; jt < 2; ++jt)
-                ka[e][jt] = *(const bf16x8*)(tile + (uint32_t)((kk >> 1) * 4096 + 2048 * jt + 512 * (kk & 1)) + o_qk);
-            };
-#pragma unroll
-            for (int kk = 0; kk < kPf; ++kk) kload(kk);
-#pragma unroll
-            for (int kk = 0; kk < 18; ++kk) {
-              if (kk + kPf < 18) kload(kk + kPf);
-              const int e = kk % (kPf + 1);
-              s[0][kk & 1] = mfma16(ka[e][0], q[kk], s[0][kk & 1]);
-              s[1][kk & 1] = mfma16(ka[e][1], q[kk], s[1][kk & 1]);
-              __builtin_amdgcn_sched_barrier(0);
-            }
-            asm volatile("s_nop 15\n\ts_nop 7" : "+v"(s[0][0]), "+v"(s[0][1]), "+v"(s[1][0]), "+v"(s[1][1]));
-            s[0][0] += s[0][1];
-            s[1][0] += s[1][1];
-            ln = fresh_lane();
-            if (nv < kSub) {  // mask the tokens past the visible end
-#pragma unroll
-              for (int jt = 0; jt < 2; ++jt)
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                  if (16 * jt + 4 * (ln >> 4) + r >= nv) s[jt][0][r] = -INFINITY;
-            }
-            // this lane's max over its 8 scores, in log2 units; the reference
-            // max moves only when a score passes it by more than 2^8
-            const float lm = fmaxf(fmaxf(fmaxf(s[0][0][0], s[0][0][1]), fmaxf(s[0][0][2], s[0][0][3])),
-                                   fmaxf(fmaxf(s[1][0][0], s[1][0][1]), fmaxf(s[1][0][2], s[1][0][3]))) * sl2;
-            need = __ballot(lm > m_run + 8.f) != 0;
-            if (need) {
-              float mt = fmaxf(lm, __shfl_xor(lm, 16, 64));
-              mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-              const float m_new = fmaxf(m_run, mt);
-              alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-              m_run = m_new;
-              l_run *= alpha;
-            }
-            const float m_use = m_run == -INFINITY ? 0.f : m_run;
-#pragma unroll
-            for (int jt = 0; jt < 2; ++jt)
-#pragma unroll
-              for (int r = 0; r < 4; ++r) {
-                const float e = __builtin_amdgcn_exp2f(fmaf(s[jt][0][r], sl2, -m_use));
-                l_run += e;
-                pw[4 * jt + r] = (__bf16)e;
-              }
-          }
-          // P rows of this wave (zeros when it has nothing to score)
-          char* pb = smem + L::kOffP + kb * L::kPBuf;
-          const uint32_t o_pw = off_pw(fresh_lane(), w);
-          *(bf16x4*)(pb + o_pw) = __builtin_shufflevector(pw, pw, 0, 1, 2, 3);
-          *(bf16x4*)(pb + o_pw + 32) = __builtin_shufflevector(pw, pw, 4, 5, 6, 7);
-          ln = fresh_lane();
-          if ((ln >> 4) == 0) alpha_buf[64 * kb + 16 * w + (ln & 15)] = alpha;
-          if (ln == 0) flags[4 * kb + w] = need ? 1 : 0;
-        }
-        if (last) {  // the segment's row totals, for the value waves
-          float l_tot = l_run + __shfl_xor(l_run, 16, 64);
-          l_tot += __shfl_xor(l_tot, 32, 64);
-          ln = fresh_lane();
-          if ((ln >> 4) == 0) {
-            invl_buf[64 * kb + 16 * w + (ln & 15)] = l_tot > 0.f ? 1.f / l_tot : 0.f;
-            lse_buf[64 * kb + 16 * w + (ln & 15)] =
-                l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
-          }
-          new_seg = true;
-        }
-        step_sub(cx, chh);
+        asm volatile("s_nop 15\n\ts_nop 7" : "+v"(sc[0]), "+v"(sc[1]));
       }
-      block_sync();
+      ln = fresh_lane();
+      if (nv < kSub) {  // mask the tokens past the visible end
+#pragma unroll
+        for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (16 * jt + 4 * (ln >> 4) + r >= nv) sc[jt][r] = -INFINITY;
+      }
+      // this lane's max over its 8 scores, in log2 units; the reference max
+      // of a row moves only when one of its scores passes it by more than 2^8
+      // (exponentials stay <= 256, and the final normalisation uses the same
+      // reference for numerator and denominator)
+      const float lm = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
+                             fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3]))) * sl2;
+      if (__ballot(lm > m_run + 8.f) != 0) {
+        float mt = fmaxf(lm, __shfl_xor(lm, 16, 64));
+        mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+        const float m_new = fmaxf(m_run, mt);
+        const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int nb = 0; nb < 32; ++nb) o[nb] *= alpha;  // lane l holds row l%16's accumulators
+      }
+      const float m_use = m_run == -INFINITY ? 0.f : m_run;
+      f16x8 p;  // P^T operand: tokens {4(l/16)..+3, 16+4(l/16)..+3} of row l%16
+#pragma unroll
+      for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float e = __builtin_amdgcn_exp2f(fmaf(sc[jt][r], sl2, -m_use));
+          l_run += e;
+          p[4 * jt + r] = (_Float16)e;
+        }
+
+      // ------------------------------------------------ O^T += V^T P^T
+      const int lv = fresh_lane();
+      const uint32_t vb00 = vt_base(lv, 0, 0), vb01 = vt_base(lv, 0, 1);
+      const uint32_t vb10 = vt_base(lv, 1, 0), vb11 = vt_base(lv, 1, 1);
+      auto vload = [&](int nb) {
+        const uint32_t cb = (uint32_t)((nb >> 2) * 4096 + (nb & 3) * 256);
+        return cath(lds_tr4h(tile, cb + ((nb & 1) ? vb01 : vb00)),
+                    lds_tr4h(tile, cb + ((nb & 1) ? vb11 : vb10)));
+      };
+      f16x8 va = vload(0), vn = vload(1);
+#pragma unroll
+      for (int nb = 0; nb < 32; ++nb) {
+        const f16x8 vnn = nb + 2 < 32 ? vload(nb + 2) : vn;
+        // this sub-tile's share of the loads of sub-tile s+3 goes out between
+        // the MFMAs, so that the issue stalls overlap the matrix core's work
+        if ((nb & 3) == 3 && more && issued < cg1) issue_cg(plan, w, issued++);
+        o[nb] = mfma16h(va, p, o[nb]);
+        __builtin_amdgcn_sched_barrier(0);
+        va = vn;
+        vn = vnn;
+      }
     }
+    if (more)
+      for (; issued < cg1; ++issued) issue_cg(plan, w, issued);  // the rest (all, without a value sum)
+
+    if (last) {  // end of this unit's part of the sequence: write the partial
+      float l_tot = l_run + __shfl_xor(l_run, 16, 64);
+      l_tot += __shfl_xor(l_tot, 32, 64);
+      const int lw = fresh_lane();
+      if (active) {
+        const int64_t sl = (int64_t)u + ci.b;
+        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+        if ((lw >> 4) == 0)
+          a.lse_part[sl * R + qrow0 + (lw & 15)] =
+              l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+        // fp16 partial row of 1 KB per query row; lane l writes columns
+        // 16 nb + 4(l/16)..+3 of row l%16
+        _Float16* prow = (_Float16*)a.o_part + (sl * R + qrow0 + (lw & 15)) * 512 + 4 * (lw >> 4);
+#pragma unroll
+        for (int nb = 0; nb < 32; ++nb) {
+          const f16x4 hv = {(_Float16)(o[nb][0] * inv), (_Float16)(o[nb][1] * inv),
+                            (_Float16)(o[nb][2] * inv), (_Float16)(o[nb][3] * inv)};
+          *(f16x4*)(prow + 16 * nb) = hv;
+        }
+      }
+#pragma unroll
+      for (int nb = 0; nb < 32; ++nb) o[nb] = f32x4{};
+      new_seg = true;
+      wait_vm0();  // keeps the hand-counted load waits exact
+    }
+    // this wave's chunks of the next sub-tile, once they have landed
+    if (s + 1 < nsub) convert_sub(s + 1, fresh_lane());
+    step_sub(cx, chh);
+    block_sync();  // sub-tile s+1 complete for everyone; slot of s free
   }
 }
 
@@ -873,8 +827,8 @@ hipError_t launch_decode_mfma(const mla_dims_t& d, const DecodeArgs& a, hipStrea
     dim3 grid((unsigned)a.num_splits, (unsigned)((R + 127) / 128));
     hipLaunchKernelGGL(decode_fp8_kernel, grid, dim3(512), 0, s, a);
   } else {
-    dim3 grid((unsigned)a.num_splits, (unsigned)((R + kHsRows - 1) / kHsRows));
-    hipLaunchKernelGGL(decode_hs_kernel, grid, dim3(512), 0, s, a);
+    dim3 grid((unsigned)a.num_splits, (unsigned)((R + kSfRows - 1) / kSfRows));
+    hipLaunchKernelGGL(decode_sf_kernel, grid, dim3(512), 0, s, a);
   }
   return hipGetLastError();
 }

@@ -14,11 +14,12 @@ namespace mla {
 // One block per query row (b, i, h); threads over latent columns, then over
 // RoPE pairs.  q_lat[c] = sum_d w_uk[h][d][c] q_nope[d]   (key absorption:
 // the content key W_UK c is never formed, its transpose moves to the query).
-template <typename T>
+// T: inputs (fp32 or bf16 bits); QA: q_abs (fp32, or fp16 for bf16 inputs).
+template <typename T, typename QA>
 __global__ __launch_bounds__(256) void absorb_generic_kernel(
     const T* __restrict__ q_nope, const T* __restrict__ q_rope,
     const int32_t* __restrict__ positions, double rope_base, const T* __restrict__ w_uk,
-    T* __restrict__ q_abs, int H, int d_n, int d_r, int d_c) {
+    QA* __restrict__ q_abs, int H, int d_n, int d_r, int d_c) {
   const int64_t row = blockIdx.x;  // ((b*Lq)+i)*H + h
   const int h = (int)(row % H);
   const int64_t bi = row / H;
@@ -28,7 +29,7 @@ __global__ __launch_bounds__(256) void absorb_generic_kernel(
     for (int d = 0; d < d_n; ++d)
       acc = fmaf(Elem<T>::load(q_nope, row * d_n + d),
                  Elem<T>::load(w_uk, ((int64_t)h * d_n + d) * d_c + c), acc);
-    Elem<T>::store(q_abs, row * W + c, acc);
+    Elem<QA>::store(q_abs, row * W + c, acc);
   }
   // RoPE: pair k turns by pos * base^(-2k/d_r); angle and its sine/cosine in fp64.
   const double pos = (double)positions[bi];
@@ -39,8 +40,8 @@ __global__ __launch_bounds__(256) void absorb_generic_kernel(
     const float x0 = Elem<T>::load(q_rope, row * d_r + 2 * k);
     const float x1 = Elem<T>::load(q_rope, row * d_r + 2 * k + 1);
     const float cs = (float)c, sn = (float)s;
-    Elem<T>::store(q_abs, row * W + d_c + 2 * k, x0 * cs - x1 * sn);
-    Elem<T>::store(q_abs, row * W + d_c + 2 * k + 1, x0 * sn + x1 * cs);
+    Elem<QA>::store(q_abs, row * W + d_c + 2 * k, x0 * cs - x1 * sn);
+    Elem<QA>::store(q_abs, row * W + d_c + 2 * k + 1, x0 * sn + x1 * cs);
   }
 }
 
@@ -175,14 +176,14 @@ hipError_t launch_absorb_generic(const mla_dims_t& d, const void* q_nope, const 
                                  void* q_abs, hipStream_t s) {
   const int64_t rows = (int64_t)d.batch * d.q_len * d.heads;
   if (d.q_dtype == MLA_F32)
-    hipLaunchKernelGGL(absorb_generic_kernel<float>, dim3((unsigned)rows), dim3(256), 0, s,
+    hipLaunchKernelGGL((absorb_generic_kernel<float, float>), dim3((unsigned)rows), dim3(256), 0, s,
                        (const float*)q_nope, (const float*)q_rope, positions, (double)rope_base,
                        (const float*)w_uk, (float*)q_abs, d.heads, d.d_nope, d.d_rope,
                        d.d_latent);
   else
-    hipLaunchKernelGGL(absorb_generic_kernel<uint16_t>, dim3((unsigned)rows), dim3(256), 0, s,
-                       (const uint16_t*)q_nope, (const uint16_t*)q_rope, positions,
-                       (double)rope_base, (const uint16_t*)w_uk, (uint16_t*)q_abs, d.heads,
+    hipLaunchKernelGGL((absorb_generic_kernel<uint16_t, _Float16>), dim3((unsigned)rows), dim3(256),
+                       0, s, (const uint16_t*)q_nope, (const uint16_t*)q_rope, positions,
+                       (double)rope_base, (const uint16_t*)w_uk, (_Float16*)q_abs, d.heads,
                        d.d_nope, d.d_rope, d.d_latent);
   return hipGetLastError();
 }
@@ -196,10 +197,10 @@ hipError_t launch_decode_generic(const mla_dims_t& d, const DecodeArgs& a, hipSt
   dim3 grid((unsigned)a.num_splits, (unsigned)((R + 3) / 4));
   if (d.q_dtype == MLA_F32)
     hipLaunchKernelGGL((decode_generic_kernel<float, float>), grid, dim3(256), 0, s, a);
-  else if (d.kv_dtype == MLA_BF16)
-    hipLaunchKernelGGL((decode_generic_kernel<uint16_t, uint16_t>), grid, dim3(256), 0, s, a);
+  else if (d.kv_dtype == MLA_BF16)  // fp16 absorbed query, bf16 cache
+    hipLaunchKernelGGL((decode_generic_kernel<_Float16, uint16_t>), grid, dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((decode_generic_kernel<uint16_t, uint8_t>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((decode_generic_kernel<_Float16, uint8_t>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -13,8 +13,13 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+typedef __fp16 fp16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) fp16x4_t lds_f16x4;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -25,6 +30,21 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 
 __device__ __forceinline__ bf16x4 lds_tr4(const char* base, uint32_t off) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)((lds_char*)base + off));
+}
+
+// fp16 forms: the decode kernels score and sum in fp16 (an exact image of
+// the bf16 or e4m3 cache values, and an 11-bit-significand query)
+__device__ __forceinline__ f32x16 mfma32h(f16x8 a, f16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16h(f16x8 a, f16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f16x4 lds_tr4h(const char* base, uint32_t off) {
+  return __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_f16x4*)((lds_char*)base + off)));
+}
+__device__ __forceinline__ f16x8 cath(f16x4 a, f16x4 b) {
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
 __device__ __forceinline__ bf16x8 cat(bf16x4 a, bf16x4 b) {
@@ -69,14 +89,6 @@ __device__ __forceinline__ int64_t uniform64(int64_t v) {
 // sees every earlier vector load as complete (and places no later waits for
 // them, which would otherwise land on the next tile's prefetch).
 __device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0f70); }
-// Scalar (SMEM) load of a wave-uniform int, waited in place.  Metadata of
-// the cache (lengths, page ids) is read this way so that no vector-memory
-// wait the compiler places for it can land on an in-flight tile prefetch.
-__device__ __forceinline__ int sload_i32(const int32_t* p) {
-  int v;
-  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
-  return v;
-}
 // s_waitcnt vmcnt(n) for n in 0..9 (tile loads still allowed in flight).
 __device__ __forceinline__ void wait_vm(int n) {
   switch (n) {

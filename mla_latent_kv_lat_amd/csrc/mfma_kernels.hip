@@ -7,6 +7,10 @@
 //          DeepSeek MLA Matrix Absorption and Memory Minimalism"
 //   [MATH] "Multi-Head Latent Attention (MLA): Mathematical Foundations, ..."
 //
+// The absorbed query q_abs is written in fp16 (saturating at +-65504): its
+// 11-bit significand is what keeps scores against long contexts with large
+// cached values accurate (a bf16 query moves such scores by ~1e-2).
+//
 // MFMA operand layouts used below (v_mfma_f32_32x32x16_bf16, wave64):
 //   A (32 x 16): lane l holds row l%32, k = 8*(l/32) .. +7
 //   B (16 x 32): lane l holds column l%32, k = 8*(l/32) .. +7
@@ -94,8 +98,8 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(
     __sincosf((float)ang, &sn, &cs);
     const float x0 = bf16_to_f32((uint16_t)(xq & 0xffffu)), x1 = bf16_to_f32((uint16_t)(xq >> 16));
     const int64_t dst = ((int64_t)m * H + h) * W + d_c + 2 * k;
-    *(uint32_t*)(q_abs + dst) = (uint32_t)f32_to_bf16(x0 * cs - x1 * sn) |
-                                ((uint32_t)f32_to_bf16(x0 * sn + x1 * cs) << 16);
+    *(uint32_t*)(q_abs + dst) = (uint32_t)f32_to_f16_sat_bits(x0 * cs - x1 * sn) |
+                                ((uint32_t)f32_to_f16_sat_bits(x0 * sn + x1 * cs) << 16);
   };
 
   // inputs of this thread's first RoPE pairs, issued first so that their
@@ -156,8 +160,9 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(
       uint16_t* dst = q_abs + ((int64_t)m * H + h) * W + cb * kAbsCols + 4 * g;
 #pragma unroll
       for (int nb = 0; nb < 8; ++nb) {
-        const uint2 v = make_uint2((uint32_t)f32_to_bf16(acc[nb][0]) | ((uint32_t)f32_to_bf16(acc[nb][1]) << 16),
-                                   (uint32_t)f32_to_bf16(acc[nb][2]) | ((uint32_t)f32_to_bf16(acc[nb][3]) << 16));
+        const uint2 v = make_uint2(
+            (uint32_t)f32_to_f16_sat_bits(acc[nb][0]) | ((uint32_t)f32_to_f16_sat_bits(acc[nb][1]) << 16),
+            (uint32_t)f32_to_f16_sat_bits(acc[nb][2]) | ((uint32_t)f32_to_f16_sat_bits(acc[nb][3]) << 16));
         *(uint2*)(dst + nb * 16) = v;
       }
     }

@@ -205,11 +205,10 @@ int mla_num_splits_hint(const mla_dims_t* dims, int32_t device, int32_t* num_spl
   int cus = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess)
     return MLA_ERR_HIP;
-  // one workgroup per (split unit, row group) on every compute unit: row
-  // groups of 64 for the bf16 cache (head-split kernel), of 128 otherwise
+  // one workgroup per (split unit, block of 128 query rows) on every
+  // compute unit
   const int rows = dims->q_len * dims->heads;
-  const int per = dims->kv_dtype == MLA_BF16 && dims->q_dtype == MLA_BF16 ? 64 : 128;
-  const int groups = (rows + per - 1) / per;
+  const int groups = (rows + 127) / 128;
   int g = cus / (groups > 0 ? groups : 1);
   *num_splits = g > 0 ? g : 1;
   return MLA_OK;

@@ -31,7 +31,9 @@ class DecodeStep:
         W = d.d_latent + d.d_rope
         n_o, n_l = _b.mla_workspace_elems(d, self.num_splits)
         kw = dict(device=self.device)
-        self.q_abs = torch.empty((B, Lq, H, W), dtype=qt, **kw)
+        # the absorbed query: fp32 on the fp32 path, fp16 for bf16 queries (mla.h)
+        self.q_abs = torch.empty((B, Lq, H, W), dtype=torch.float32 if d.q_dtype == _b.F32
+                                 else torch.float16, **kw)
         # normalised partials: fp32 on the fp32 path, fp16 otherwise (mla.h)
         pt = torch.float32 if d.q_dtype == _b.F32 else torch.float16
         self.o_part = torch.empty(max(n_o, 1), dtype=pt, **kw)
