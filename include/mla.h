@@ -49,7 +49,8 @@ enum {
   MLA_ERR_INVALID_ARG = 1, /* NULL pointer, bad size, misalignment, bad enum  */
   MLA_ERR_UNSUPPORTED = 2, /* valid but not built (dtype mix, width limits)   */
   MLA_ERR_WORKSPACE = 3,   /* workspace pointers missing                     */
-  MLA_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed     */
+  MLA_ERR_HIP = 4,         /* a HIP runtime call or kernel launch failed     */
+  MLA_ERR_TOO_LARGE = 5    /* request exceeds a fixed internal buffer        */
 };
 
 /* Element types. */
@@ -280,6 +281,29 @@ int mla_kv_append(const mla_append_dims_t* dims, const void* h, const void* w_dk
                   float rope_base, float eps, const int64_t* cache_rows, void* latent_cache,
                   void* rope_cache, int64_t kv_row_stride, float* kv_scale, void* workspace,
                   void* stream);
+
+/*
+ * mla_kv_append_noalloc -- mla_kv_append without a workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation).
+ *
+ * Same arguments, results and validation as mla_kv_append; the partial sums
+ * go to a static device array of MLA_KV_APPEND_NOALLOC_SCRATCH_BYTES bytes
+ * that every GPU the library runs on holds until the process ends.  A call
+ * whose mla_kv_append_workspace_bytes() exceeds that size returns
+ * MLA_ERR_TOO_LARGE before anything is enqueued (8 MiB: e.g. 260 new tokens
+ * at hidden width 7168).  The first call on a GPU looks the array's device
+ * address up on the current device (nothing is allocated, ever); call it
+ * with the stream's device current.  All calls on one GPU share the array:
+ * calls that overlap in time on one GPU (other streams, other threads)
+ * race and must be serialised by the caller.
+ */
+#define MLA_KV_APPEND_NOALLOC_SCRATCH_BYTES (8 << 20)
+int mla_kv_append_noalloc(const mla_append_dims_t* dims, const void* h, const void* w_dkv,
+                          const void* kv_norm_w, const void* w_kr, const int32_t* positions,
+                          float rope_base, float eps, const int64_t* cache_rows,
+                          void* latent_cache, void* rope_cache, int64_t kv_row_stride,
+                          float* kv_scale, void* stream);
 
 #ifdef __cplusplus
 }

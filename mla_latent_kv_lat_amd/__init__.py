@@ -7,7 +7,8 @@ cache-append producer that writes each new token's cache row.
 """
 
 from .binding import (BF16, F32, FLAG_GENERIC, FP8_E4M3, TILE_TOKENS, MLAAppendDims, MLADims,
-                      MLAError, append_dims, dims, mla_kv_append, mla_kv_append_workspace_bytes,
+                      MLAError, append_dims, dims, mla_kv_append, mla_kv_append_noalloc,
+                      mla_kv_append_workspace_bytes,
                       mla_absorb_q, mla_combine, mla_combine_out_proj, mla_decode_attn, mla_num_splits_hint,
                       mla_out_proj, mla_split_plan, mla_workspace_bytes,
                       mla_workspace_elems)
@@ -15,7 +16,7 @@ from .step import DecodeStep
 
 __all__ = [
     "BF16", "F32", "FLAG_GENERIC", "FP8_E4M3", "TILE_TOKENS", "MLAAppendDims", "MLADims", "MLAError",
-    "append_dims", "dims", "mla_kv_append", "mla_kv_append_workspace_bytes",
+    "append_dims", "dims", "mla_kv_append", "mla_kv_append_noalloc", "mla_kv_append_workspace_bytes",
     "mla_absorb_q", "mla_combine", "mla_combine_out_proj", "mla_decode_attn", "mla_num_splits_hint", "mla_out_proj",
     "mla_split_plan", "mla_workspace_bytes", "mla_workspace_elems", "DecodeStep",
 ]

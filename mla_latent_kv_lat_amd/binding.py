@@ -25,8 +25,10 @@ F32, BF16, FP8_E4M3 = 0, 1, 2
 FLAG_GENERIC = 1
 TILE_TOKENS = 64
 
+KV_APPEND_NOALLOC_SCRATCH_BYTES = 8 << 20  # MLA_KV_APPEND_NOALLOC_SCRATCH_BYTES
+
 STATUS = {0: "MLA_OK", 1: "MLA_ERR_INVALID_ARG", 2: "MLA_ERR_UNSUPPORTED",
-          3: "MLA_ERR_WORKSPACE", 4: "MLA_ERR_HIP"}
+          3: "MLA_ERR_WORKSPACE", 4: "MLA_ERR_HIP", 5: "MLA_ERR_TOO_LARGE"}
 
 
 class MLAError(RuntimeError):
@@ -66,6 +68,8 @@ def _load():
         "mla_kv_append_workspace_bytes": [ctypes.POINTER(MLAAppendDims), ctypes.POINTER(I64)],
         "mla_kv_append": [ctypes.POINTER(MLAAppendDims), VP, VP, VP, VP, VP, F, F, VP, VP, VP,
                           I64, VP, VP, VP],
+        "mla_kv_append_noalloc": [ctypes.POINTER(MLAAppendDims), VP, VP, VP, VP, VP, F, F, VP, VP,
+                                  VP, I64, VP, VP],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -201,3 +205,13 @@ def mla_kv_append(d: MLAAppendDims, h, w_dkv, kv_norm_w, w_kr, positions, rope_b
                               _ptr(latent_cache), _ptr(rope_cache), int(kv_row_stride),
                               _ptr(kv_scale), _ptr(workspace), _stream(stream)),
            "mla_kv_append")
+
+
+def mla_kv_append_noalloc(d: MLAAppendDims, h, w_dkv, kv_norm_w, w_kr, positions, rope_base, eps,
+                          cache_rows, latent_cache, rope_cache, kv_row_stride, kv_scale,
+                          stream=None):
+    _check(_lib.mla_kv_append_noalloc(ctypes.byref(d), _ptr(h), _ptr(w_dkv), _ptr(kv_norm_w),
+                                      _ptr(w_kr), _ptr(positions), float(rope_base), float(eps),
+                                      _ptr(cache_rows), _ptr(latent_cache), _ptr(rope_cache),
+                                      int(kv_row_stride), _ptr(kv_scale), _stream(stream)),
+           "mla_kv_append_noalloc")

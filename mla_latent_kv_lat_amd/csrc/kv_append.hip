@@ -35,6 +35,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "common.hpp"
 #include "../../include/mla.h"
 
@@ -222,6 +224,84 @@ bool app_dims_ok(const mla_append_dims_t* d) {
   return d && d->n_tokens >= 0 && d->d_model > 0 && d->d_latent > 0 && d->d_rope >= 0;
 }
 
+// Host validation shared by both entry points: 0, or the status to return.
+int app_check(const mla_append_dims_t* dims, const void* h, const void* w_dkv,
+              const void* kv_norm_w, const void* w_kr, const int32_t* positions, float rope_base,
+              float eps, const int64_t* cache_rows, const void* latent_cache,
+              const void* rope_cache, int64_t kv_row_stride, const float* kv_scale) {
+  if (!app_dims_ok(dims)) return MLA_ERR_INVALID_ARG;
+  if (dims->d_latent != kAppLat || dims->d_rope != kAppN - kAppLat || dims->d_model % kAppChunk ||
+      dims->d_model > kAppChunk * kAppMaxChunks ||
+      (dims->kv_dtype != MLA_BF16 && dims->kv_dtype != MLA_FP8_E4M3))
+    return MLA_ERR_UNSUPPORTED;
+  if (dims->n_tokens == 0) return MLA_OK;
+  const bool f8 = dims->kv_dtype == MLA_FP8_E4M3;
+  if (!h || !w_dkv || !kv_norm_w || !w_kr || !positions || !cache_rows || !latent_cache ||
+      !rope_cache || (kv_scale != nullptr) != f8)
+    return MLA_ERR_INVALID_ARG;
+  auto al = [](const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; };
+  if (!al(h, 16) || !al(w_dkv, 16) || !al(w_kr, 16) || !al(kv_norm_w, 16) ||
+      !al(latent_cache, f8 ? 8 : 16) || !al(rope_cache, f8 ? 2 : 4) || (f8 && !al(kv_scale, 4)))
+    return MLA_ERR_INVALID_ARG;
+  if (kv_row_stride < kAppLat || kv_row_stride % 8) return MLA_ERR_INVALID_ARG;
+  if (!(rope_base > 0.f) || !isfinite(rope_base) || !(eps >= 0.f) || !isfinite(eps))
+    return MLA_ERR_INVALID_ARG;
+  return MLA_OK;
+}
+
+// The two kernels in turn; `workspace` holds the partial sums (16-byte aligned).
+int app_launch(const mla_append_dims_t* dims, const void* h, const void* w_dkv,
+               const void* kv_norm_w, const void* w_kr, const int32_t* positions, float rope_base,
+               float eps, const int64_t* cache_rows, void* latent_cache, void* rope_cache,
+               int64_t kv_row_stride, float* kv_scale, float* workspace, hipStream_t s) {
+  const bool f8 = dims->kv_dtype == MLA_FP8_E4M3;
+  (void)hipGetLastError();
+  const int chunks = dims->d_model / kAppChunk;
+  const int items = (kAppN / 32) * chunks;
+  hipLaunchKernelGGL(kv_down_kernel, dim3(8 * ((items + 7) / 8)), dim3(256), 0, s,
+                     (const uint16_t*)h, (const uint16_t*)w_dkv, (const uint16_t*)w_kr,
+                     dims->n_tokens, dims->d_model, chunks, workspace);
+  if (hipGetLastError() != hipSuccess) return MLA_ERR_HIP;
+  const dim3 fg(dims->n_tokens);
+  if (f8)
+    hipLaunchKernelGGL(kv_finish_kernel<true>, fg, dim3(64), 0, s, (const float*)workspace,
+                       chunks, dims->n_tokens, (const uint16_t*)kv_norm_w, positions,
+                       log2((double)rope_base), eps, cache_rows, (char*)latent_cache,
+                       (char*)rope_cache, kv_row_stride, kv_scale);
+  else
+    hipLaunchKernelGGL(kv_finish_kernel<false>, fg, dim3(64), 0, s, (const float*)workspace,
+                       chunks, dims->n_tokens, (const uint16_t*)kv_norm_w, positions,
+                       log2((double)rope_base), eps, cache_rows, (char*)latent_cache,
+                       (char*)rope_cache, kv_row_stride * 2, nullptr);
+  return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+// Scratch of mla_kv_append_noalloc: kv_down_kernel's fp32 partial sums in
+// a file-scope device array, one copy per GPU the library runs on, held
+// until the process ends.  Host code never passes `scratch` itself (its
+// host-side name is only a stand-in for the device object): the device
+// address comes from hipGetSymbolAddress, once per device.
+constexpr int64_t kAppScratchBytes = MLA_KV_APPEND_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) float scratch[kAppScratchBytes / 4];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch_ptr[kMaxDevices];  // device address of `scratch` per device (null: not looked up)
+
+// The device address of `scratch` on the current device, looked up on the
+// first call on that device (with it current).  Null on failure.
+float* scratch_on_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    g_scratch_ptr[dev] = (float*)ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
 }  // namespace
 }  // namespace mla
 
@@ -243,44 +323,31 @@ int mla_kv_append(const mla_append_dims_t* dims, const void* h, const void* w_dk
                   float rope_base, float eps, const int64_t* cache_rows, void* latent_cache,
                   void* rope_cache, int64_t kv_row_stride, float* kv_scale, void* workspace,
                   void* stream) {
-  if (!app_dims_ok(dims)) return MLA_ERR_INVALID_ARG;
-  if (dims->d_latent != kAppLat || dims->d_rope != kAppN - kAppLat || dims->d_model % kAppChunk ||
-      dims->d_model > kAppChunk * kAppMaxChunks ||
-      (dims->kv_dtype != MLA_BF16 && dims->kv_dtype != MLA_FP8_E4M3))
-    return MLA_ERR_UNSUPPORTED;
-  if (dims->n_tokens == 0) return MLA_OK;
-  const bool f8 = dims->kv_dtype == MLA_FP8_E4M3;
-  if (!h || !w_dkv || !kv_norm_w || !w_kr || !positions || !cache_rows || !latent_cache ||
-      !rope_cache || (kv_scale != nullptr) != f8)
-    return MLA_ERR_INVALID_ARG;
+  const int st = app_check(dims, h, w_dkv, kv_norm_w, w_kr, positions, rope_base, eps, cache_rows,
+                           latent_cache, rope_cache, kv_row_stride, kv_scale);
+  if (st != MLA_OK || dims->n_tokens == 0) return st;
   if (!workspace) return MLA_ERR_WORKSPACE;
-  auto al = [](const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; };
-  if (!al(h, 16) || !al(w_dkv, 16) || !al(w_kr, 16) || !al(kv_norm_w, 16) || !al(workspace, 16) ||
-      !al(latent_cache, f8 ? 8 : 16) || !al(rope_cache, f8 ? 2 : 4) || (f8 && !al(kv_scale, 4)))
-    return MLA_ERR_INVALID_ARG;
-  if (kv_row_stride < kAppLat || kv_row_stride % 8) return MLA_ERR_INVALID_ARG;
-  if (!(rope_base > 0.f) || !isfinite(rope_base) || !(eps >= 0.f) || !isfinite(eps))
-    return MLA_ERR_INVALID_ARG;
-  hipStream_t s = (hipStream_t)stream;
-  (void)hipGetLastError();
-  const int chunks = dims->d_model / kAppChunk;
-  const int items = (kAppN / 32) * chunks;
-  hipLaunchKernelGGL(kv_down_kernel, dim3(8 * ((items + 7) / 8)), dim3(256), 0, s,
-                     (const uint16_t*)h, (const uint16_t*)w_dkv, (const uint16_t*)w_kr,
-                     dims->n_tokens, dims->d_model, chunks, (float*)workspace);
-  if (hipGetLastError() != hipSuccess) return MLA_ERR_HIP;
-  const dim3 fg(dims->n_tokens);
-  if (f8)
-    hipLaunchKernelGGL(kv_finish_kernel<true>, fg, dim3(64), 0, s, (const float*)workspace,
-                       chunks, dims->n_tokens, (const uint16_t*)kv_norm_w, positions,
-                       log2((double)rope_base), eps, cache_rows, (char*)latent_cache,
-                       (char*)rope_cache, kv_row_stride, kv_scale);
-  else
-    hipLaunchKernelGGL(kv_finish_kernel<false>, fg, dim3(64), 0, s, (const float*)workspace,
-                       chunks, dims->n_tokens, (const uint16_t*)kv_norm_w, positions,
-                       log2((double)rope_base), eps, cache_rows, (char*)latent_cache,
-                       (char*)rope_cache, kv_row_stride * 2, nullptr);
-  return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+  if (((uintptr_t)workspace & 15) != 0) return MLA_ERR_INVALID_ARG;
+  return app_launch(dims, h, w_dkv, kv_norm_w, w_kr, positions, rope_base, eps, cache_rows,
+                    latent_cache, rope_cache, kv_row_stride, kv_scale, (float*)workspace,
+                    (hipStream_t)stream);
+}
+
+int mla_kv_append_noalloc(const mla_append_dims_t* dims, const void* h, const void* w_dkv,
+                          const void* kv_norm_w, const void* w_kr, const int32_t* positions,
+                          float rope_base, float eps, const int64_t* cache_rows,
+                          void* latent_cache, void* rope_cache, int64_t kv_row_stride,
+                          float* kv_scale, void* stream) {
+  const int st = app_check(dims, h, w_dkv, kv_norm_w, w_kr, positions, rope_base, eps, cache_rows,
+                           latent_cache, rope_cache, kv_row_stride, kv_scale);
+  if (st != MLA_OK || dims->n_tokens == 0) return st;
+  // the partial sums must fit the static scratch
+  const int64_t need = (int64_t)(dims->d_model / kAppChunk) * dims->n_tokens * kAppN * 4;
+  if (need > kAppScratchBytes) return MLA_ERR_TOO_LARGE;
+  float* ws = scratch_on_current_device();
+  if (!ws) return MLA_ERR_HIP;
+  return app_launch(dims, h, w_dkv, kv_norm_w, w_kr, positions, rope_base, eps, cache_rows,
+                    latent_cache, rope_cache, kv_row_stride, kv_scale, ws, (hipStream_t)stream);
 }
 
 }  // extern "C"

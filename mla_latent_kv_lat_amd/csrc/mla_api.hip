@@ -45,6 +45,7 @@ const char* mla_status_string(int status) {
     case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED: combination not built";
     case MLA_ERR_WORKSPACE: return "MLA_ERR_WORKSPACE: split-K workspace missing";
     case MLA_ERR_HIP: return "MLA_ERR_HIP: HIP runtime or launch failure";
+    case MLA_ERR_TOO_LARGE: return "MLA_ERR_TOO_LARGE: request exceeds a fixed internal buffer";
     default: return "unknown MLA status";
   }
 }

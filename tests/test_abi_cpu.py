@@ -30,7 +30,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_status_strings():
     lib = binding.library()
-    for code in range(5):
+    for code in range(6):
         assert lib.mla_status_string(code).decode().startswith("MLA_")
 
 
@@ -178,3 +178,34 @@ def test_kv_append_validation():
     assert call(d, eps=float("nan")) == 1
     assert call(d, kv_scale=16) == 1
     assert lib.mla_kv_append_workspace_bytes(None, ctypes.byref(ws)) == 1
+
+
+def test_kv_append_noalloc_validation():
+    """The static-scratch variant: the same host checks, and requests beyond
+    its fixed buffer rejected before anything touches the GPU."""
+    lib = binding._lib
+    ok = dict(h=16, w_dkv=16, kv_norm_w=16, w_kr=16, positions=16, rope_base=10000.0, eps=1e-6,
+              cache_rows=16, latent_cache=16, rope_cache=16, kv_row_stride=576, kv_scale=None)
+
+    def call(dd, **kw):
+        a = dict(ok, **kw)
+        return lib.mla_kv_append_noalloc(ctypes.byref(dd), a["h"], a["w_dkv"], a["kv_norm_w"],
+                                         a["w_kr"], a["positions"], a["rope_base"], a["eps"],
+                                         a["cache_rows"], a["latent_cache"], a["rope_cache"],
+                                         a["kv_row_stride"], a["kv_scale"], None)
+
+    limit = binding.KV_APPEND_NOALLOC_SCRATCH_BYTES
+    # the largest batch that fits at width 7168: 14 chunks x n x 576 fp32
+    n_max = limit // (14 * 576 * 4)
+    assert n_max == 260
+    assert call(mla.append_dims(n_max + 1, 7168)) == 5    # MLA_ERR_TOO_LARGE
+    assert call(mla.append_dims(4096, 16384)) == 5
+    assert call(mla.append_dims(4, 7000)) == 2
+    assert call(mla.append_dims(0, 7168)) == 0
+    d = mla.append_dims(4, 7168)
+    assert call(d, h=None) == 1
+    assert call(d, h=8) == 1
+    assert call(d, kv_row_stride=100) == 1
+    assert call(mla.append_dims(4, 7168, kv_dtype=mla.FP8_E4M3)) == 1
+    assert "MLA_ERR_TOO_LARGE" in lib.mla_status_string(5).decode()
+
