@@ -339,7 +339,7 @@ def main():
 
     traffic = None
     util = None
-    dec_kernel = "decode_fp8_kernel" if cfg.kv_dtype == "fp8" else "decode_hs_kernel"
+    dec_kernel = "decode_fp8_kernel" if cfg.kv_dtype == "fp8" else "decode_sf_kernel"
     tpath = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
                          "decode_hs_b64_l8k_paged_counters.json")
     if os.path.exists(tpath):
@@ -386,11 +386,13 @@ def main():
                    "launch": "HIP graph replay, one step of three kernels per replay, rotating over "
                              "the layer copies; median step (eager time beside)"},
         "kernels_us": {"absorb_q": round(kern_ms[0] * 1e3, 2), "decode_attn": round(kern_ms[1] * 1e3, 2),
-                       "combine_out_proj": round(kern_ms[2] * 1e3, 2)},
+                       "combine_out_proj": round(kern_ms[2] * 1e3, 2),
+                       "timing": "events around each launch of eager steps (median)"},
         "kv_append": kv_app,
         "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(dec_gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
-                     "kernel": dec_kernel,
+                     "kernel": dec_kernel, "launch_us": round(kern_ms[1] * 1e3, 2),
+                     "timing": "median of events around each decode launch of the eager steps, on its stream",
                      "mfma_tflops": round(dec_tflops, 1),
                      "mfma_frac": round(dec_tflops / PEAK_BF16_TFLOPS, 4),
                      "counters": util},
