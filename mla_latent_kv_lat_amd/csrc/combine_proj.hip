@@ -8,15 +8,17 @@
 //
 // One workgroup of 8 waves per (head h, 32 or 64 query rows m = (b, i));
 // wave w owns rows w, w + 8, w + 16, ... in phases 0-1:
-//   phase 0  the split-K units that touched each row's sequence b (from one
-//            prefix pass over seq_lens per workgroup) and the log-sum-exp of
-//            their partials, lse = log sum_u exp(lse_u); lane k of the wave
-//            keeps the weight exp(lse_u - lse) of the row's k-th unit;
+//   phase 0  each wave on its own: the split-K units that touched each of
+//            its rows' sequence b (a lane scan over seq_lens, whose load is
+//            the kernel's first), then the log-sum-exp of their partials,
+//            lse = log sum_u exp(lse_u); lane k of the wave keeps the weight
+//            exp(lse_u - lse) of the row's k-th unit;
 //   phase 1  o_lat = sum_u exp(lse_u - lse) o_u ([MATH] value absorption:
 //            softmax weights on the cached latents), rounded to bf16 into an
 //            LDS tile (and to memory when asked for).  The partial loads of
 //            all four rows are issued together with their LSE loads, so a
-//            row spanning up to kCPChunk units costs one memory round trip;
+//            row spanning up to kCPChunk units costs one memory round trip
+//            after the one for seq_lens; W_UV streams in meanwhile;
 //   phase 2  o = o_lat W_UV[h]^T on v_mfma_f32_32x32x16_bf16 ([ARCH] 3.2):
 //            wave w takes the 32 v-columns 32 (w & 3) + 128 j and half w >> 2
 //            of the 512 latent columns, with its rows of W_UV[h] loaded into
@@ -47,6 +49,11 @@ constexpr int kCPChunk = 4;     // partials per row loaded per pass
 __device__ inline float lane_value(float v, int k) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), k));
 }
+__device__ inline int64_t lane_i64(int64_t v, int k) {  // k wave-uniform
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, k);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)((uint64_t)v >> 32), k);
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
 
 // ROWS query rows per workgroup; VS workgroups (blockIdx.z = vpart) share a head's
 // v-columns when one row block holds every row, so that W_UV[h] is pulled
@@ -62,9 +69,6 @@ __global__ __launch_bounds__(512) void combine_proj_kernel(
   // v-column blocks per pass and latent parts per block: 4 x 2 or 2 x 4 waves
   constexpr int kNC = 4 / VS, kNK = kCPWaves / kNC, kSteps = 32 / kNK;
   __shared__ __attribute__((aligned(16))) float red[(kNK - 1) * kNC * 64 * 16];
-  __shared__ int64_t row_u0[ROWS], row_slot[ROWS];
-  __shared__ int row_n[ROWS];
-  __shared__ int64_t tot_T;
 
   constexpr int kRowsPerWave = ROWS / kCPWaves;
   const int h = blockIdx.x;
@@ -76,8 +80,14 @@ __global__ __launch_bounds__(512) void combine_proj_kernel(
   const int cq = w % kNC, kh = w / kNC;
   const int hf = lane >> 5, n32 = lane & 31;
 
-  // W_UV[h] rows 32 (kNC vpart + cq) + n32, latent part kh: in flight during
-  // phase 1
+  // ---- phase 0, by every wave for its own rows (no barrier): the lengths
+  // of the first 64 sequences load first.  With 32 rows W_UV[h] rows
+  // 32 (kNC vpart + cq) + n32 of latent part kh stream in behind them; with
+  // 64 rows the partials are twice the bytes and go first (measured 30.0
+  // against 34.2 us at 128 rows).
+  constexpr bool kWeightsFirst = ROWS <= 32;
+  const int len0 = seq_lens[lane < B ? lane : B - 1];
+  __builtin_amdgcn_sched_barrier(0);  // the load above stays ahead of the weights: its wait leaves them in flight
   bf16x8 bw[kSteps];
   auto load_w = [&]() {
     const int vb = 32 * (kNC * vpart + cq);
@@ -85,61 +95,31 @@ __global__ __launch_bounds__(512) void combine_proj_kernel(
 #pragma unroll
     for (int k = 0; k < kSteps; ++k) bw[k] = bp[2 * (kSteps * kh + k) + hf];
   };
-  // With 32 rows the weights go out first: waves 1-7 start their loads
-  // while wave 0 works out the rows' units (then issues its own), so the
-  // CU's inflow is busy through that pass (19.8 -> 19.2 us at 64 sequences).
-  // With 64 rows the partials are twice the bytes and must not queue behind
-  // the weights (measured 53.4 -> 57.4 us at 256 rows), so they go first.
-  constexpr bool kWeightsFirst = ROWS <= 32;
-  if (kWeightsFirst && w != 0) load_w();
-
-  // ---- phase 0a, by wave 0: total tiles T, then for each of the rows
-  // (lane j) its sequence's first split unit u0, unit count n and first
-  // partial slot (u0 + b) R + r
-  const int b_lo = mb0 / Lq;
-  const int nb = mb0 < M ? (min(M, mb0 + ROWS) - 1) / Lq - b_lo + 1 : 0;  // <= ROWS <= 64
-  if (w == 0) {
-    int64_t tot = 0, before = 0;
-#pragma unroll 4
-    for (int bb = lane; bb < B; bb += 64) {
-      const int64_t t = tiles_of(seq_lens[bb]);
-      tot += t;
-      before += bb < b_lo ? t : 0;
-    }
-    const int64_t mine = lane < nb ? tiles_of(seq_lens[b_lo + lane]) : 0;
-    int64_t incl = mine;
+  if (kWeightsFirst) load_w();
+  // total tiles T, and in lane i < kRowsPerWave the first tile pb and tile
+  // count tb of the sequence of this wave's row i (a lane scan per 64
+  // sequences); the rows' unit arithmetic below then runs once, in lanes
+  const int m_l = mb0 + w + kCPWaves * (lane < kRowsPerWave ? lane : 0);
+  const int b_l = (m_l < M ? m_l : M - 1) / Lq;
+  int64_t pb_l = 0, tb_l = 0, T = 0;
+  auto scan_chunk = [&](int c0, int len) {  // sequences c0 .. c0 + 63, lane bb - c0 holds len(bb)
+    const int64_t t = c0 + lane < B ? tiles_of(len) : 0;
+    int64_t incl = t;
 #pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {  // inclusive prefix over up to 64 sequences
+    for (int d = 1; d < 64; d <<= 1) {
       const int64_t x = __shfl_up(incl, d, 64);
       if (lane >= d) incl += x;
     }
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) {
-      tot += __shfl_xor(tot, d, 64);
-      before += __shfl_xor(before, d, 64);
+    const int src = b_l - c0;
+    const int64_t e = __shfl(incl - t, src & 63, 64), tt = __shfl(t, src & 63, 64);
+    if (src >= 0 && src < 64) {
+      pb_l = T + e;
+      tb_l = tt;
     }
-    const int64_t pb_mine = before + incl - mine;  // first tile of sequence b_lo + lane
-    // lane j: row m = mb0 + j
-    const int m = mb0 + lane;
-    const bool live = lane < ROWS && m < M;
-    const int b = live ? m / Lq : b_lo;
-    const int64_t pb = __shfl(pb_mine, b - b_lo, 64), tb = __shfl(mine, b - b_lo, 64);
-    int64_t u0 = 0;
-    int n = 0;
-    if (live && tb > 0) {
-      u0 = unit_of_tile(pb, tot, G);
-      n = (int)(unit_of_tile(pb + tb - 1, tot, G) - u0 + 1);
-    }
-    if (lane < ROWS) {
-      row_u0[lane] = u0;
-      row_n[lane] = n;
-      row_slot[lane] = (u0 + b) * R + (live ? (m % Lq) * H + h : h);
-    }
-    if (lane == 0) tot_T = tot;
-    if (kWeightsFirst) load_w();
-  }
-  block_sync();  // no wait on the weight loads in flight
-  const int64_t T = tot_T;
+    T += lane_i64(incl, 63);
+  };
+  scan_chunk(0, len0);
+  for (int c0 = 64; c0 < B; c0 += 64) scan_chunk(c0, seq_lens[c0 + lane < B ? c0 + lane : B - 1]);
   // with G <= T no unit is empty
   const bool may_be_empty = G > T;
   const bool small = T * (int64_t)G < ((int64_t)1 << 32);
@@ -149,9 +129,24 @@ __global__ __launch_bounds__(512) void combine_proj_kernel(
                        ((uint32_t)u * (uint32_t)T + (uint32_t)T) / (uint32_t)G
                  : unit_begin(u, T, G) < unit_begin(u + 1, T, G);
   };
+  auto unit_of = [&](int64_t x) -> int64_t {  // unit holding tile x
+    return small ? (int64_t)(((uint32_t)x * (uint32_t)G + (uint32_t)G - 1u) / (uint32_t)T)
+                 : unit_of_tile(x, T, G);
+  };
+  // lane i: row i's first unit u0, unit count n and first partial slot
+  // (u0 + b) R + r
+  int64_t u0_l = 0;
+  int n_l = 0;
+  if (m_l < M && tb_l > 0) {
+    u0_l = unit_of(pb_l);
+    n_l = (int)(unit_of(pb_l + tb_l - 1) - u0_l + 1);
+  }
+  const int64_t slot_l = (u0_l + b_l) * R + (m_l < M ? (m_l % Lq) * H + h : h);
 
-  // ---- phase 0b: the first loads of this wave's rows (what an empty unit
-  // holds is never used), then W_UV
+  // ---- the rows' LSEs and first kCPChunk partials.  The partial loads are
+  // buffer loads bounded to the row's units: a chunk past them reads zeros
+  // without touching memory (the kernel is bound by the bytes each CU pulls
+  // in), and no branch splits the loads
   const int c = 8 * lane;  // latent columns of this lane in phase 1
   int64_t u0[kRowsPerWave], slot0[kRowsPerWave];
   int n[kRowsPerWave];
@@ -159,16 +154,17 @@ __global__ __launch_bounds__(512) void combine_proj_kernel(
   h8 v[kRowsPerWave][kCPChunk];
 #pragma unroll
   for (int i = 0; i < kRowsPerWave; ++i) {
-    const int j = w + kCPWaves * i;
-    u0[i] = uniform64(row_u0[j]);
-    n[i] = __builtin_amdgcn_readfirstlane(row_n[j]);
-    slot0[i] = uniform64(row_slot[j]);
+    u0[i] = lane_i64(u0_l, i);
+    n[i] = __builtin_amdgcn_readlane(n_l, i);
+    slot0[i] = lane_i64(slot_l, i);
     lv[i] = lse_part[slot0[i] + (int64_t)(lane < n[i] ? lane : 0) * R];
-    // only the units the row's sequence crossed (n is wave-uniform): the
-    // kernel is bound by the bytes each CU pulls in, so no duplicate loads
+    const int nk = n[i] < kCPChunk ? n[i] : kCPChunk;
+    const __amdgpu_buffer_rsrc_t rs =
+        buffer_rsrc((void*)(o_part + slot0[i] * 512), nk > 0 ? ((uint32_t)(nk - 1) * (uint32_t)R + 1u) * 1024u : 0u);
 #pragma unroll
     for (int k = 0; k < kCPChunk; ++k)
-      v[i][k] = k < n[i] ? *(const h8*)(o_part + (slot0[i] + (int64_t)k * R) * 512 + c) : h8{};
+      v[i][k] = __builtin_bit_cast(h8, __builtin_amdgcn_raw_buffer_load_b128(
+                                           rs, (int)((uint32_t)k * (uint32_t)R * 1024u + 2u * c), 0, 0));
   }
   if (!kWeightsFirst) load_w();
 
@@ -290,7 +286,9 @@ __global__ __launch_bounds__(512) void combine_proj_kernel(
 }  // namespace
 
 bool combine_proj_supports(const mla_dims_t& d) {
-  return d.q_dtype == MLA_BF16 && d.d_latent == 512 && d.d_v % 32 == 0;
+  // Lq H <= 2^20 keeps the buffer ranges of a row's first partials in 32 bits
+  return d.q_dtype == MLA_BF16 && d.d_latent == 512 && d.d_v % 32 == 0 &&
+         (int64_t)d.q_len * d.heads <= (1 << 20);
 }
 
 hipError_t launch_combine_proj(const mla_dims_t& d, int num_splits, const int32_t* seq_lens,

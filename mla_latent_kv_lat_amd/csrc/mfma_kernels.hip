@@ -67,14 +67,15 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(
   const int ksteps = (d_n + 31) / 32;
   // B operand (q rows m = mb + lane%16, k 8(lane/16).. of each 32-step);
   // the first block's loads go out together with the W loads below
+  // (unconditional loads from clamped indices: a row past M is never
+  // stored, and a k past d_n meets a zero row of W)
   auto load_q = [&](int mb, bf16x8 (&qb)[kAbsMaxDn / 32]) {
-    const int m = mb + li;
+    const int m = min(mb + li, M - 1);
 #pragma unroll
     for (int ks = 0; ks < kAbsMaxDn / 32; ++ks) {
-      const int k0 = 32 * ks + 8 * g;
-      qb[ks] = (m < M && ks < ksteps && k0 < d_n)
-                   ? *(const bf16x8*)(q_nope + ((int64_t)m * H + h) * d_n + k0)
-                   : bf16x8{};
+      const int k0 = min(32 * ks + 8 * g, d_n - 8);
+      if (ks < ksteps)  // uniform
+        qb[ks] = *(const bf16x8*)(q_nope + ((int64_t)m * H + h) * d_n + k0);
     }
   };
   bf16x8 qb[kAbsMaxDn / 32];
@@ -103,14 +104,19 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(
   };
 
   // inputs of this thread's first RoPE pairs, issued first so that their
-  // arithmetic below overlaps the W_UK and q loads
+  // arithmetic below overlaps the W_UK and q loads; the loads are
+  // unconditional (indices clamped) so that no branch puts a wait between
+  // them and the W_UK loads
+  if (np > 0) {  // uniform
 #pragma unroll
-  for (int j = 0; j < kRopeAhead; ++j) {
-    const int pj = rp[j] < np ? rp[j] : 0;
-    const int m = half > 0 ? pj / half : 0, k = half > 0 ? pj % half : 0;
-    rpos[j] = rp[j] < np ? positions[m] : 0;
-    rq[j] = rp[j] < np ? *(const uint32_t*)(q_rope + ((int64_t)m * H + h) * d_r + 2 * k) : 0u;
+    for (int j = 0; j < kRopeAhead; ++j) {
+      const int pj = rp[j] < np ? rp[j] : np - 1;
+      const int m = pj / half, k = pj % half;
+      rpos[j] = positions[m];
+      rq[j] = *(const uint32_t*)(q_rope + ((int64_t)m * H + h) * d_r + 2 * k);
+    }
   }
+  __builtin_amdgcn_sched_barrier(0);
 
   // stage W_UK[h][:, cb*128 .. +128]: thread reads chunk tid%16 of rows
   // tid/16 + 16i; rows past d_n are zero (they meet zero-padded k of q)
@@ -118,12 +124,12 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(
     const char* wsrc = (const char*)(w_uk + (int64_t)h * d_n * d_c + cb * kAbsCols);
     uint4 st[kAbsMaxDn / 16];
 #pragma unroll
-    for (int i = 0; i < kAbsMaxDn / 16; ++i) {
-      const int r = (tid >> 4) + 16 * i;
-      st[i] = r < d_n ? *(const uint4*)(wsrc + (int64_t)r * d_c * 2 + (tid & 15) * 16)
-                      : make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < kAbsMaxDn / 16; ++i) {  // rows clamped here, zeroed at the LDS store
+      const int r = min((tid >> 4) + 16 * i, d_n - 1);
+      st[i] = *(const uint4*)(wsrc + (int64_t)r * d_c * 2 + (tid & 15) * 16);
     }
     load_q(16 * w, qb);
+    __builtin_amdgcn_sched_barrier(0);
 
     // RoPE pairs of this head, spread over its column-block workgroups
 #pragma unroll
@@ -134,8 +140,10 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(
                 *(const uint32_t*)(q_rope + ((int64_t)(p / half) * H + h) * d_r + 2 * (p % half)));
 
 #pragma unroll
-    for (int i = 0; i < kAbsMaxDn / 16; ++i)
-      *(uint4*)(wsm + ((tid >> 4) + 16 * i) * kAbsPitch + (tid & 15) * 16) = st[i];
+    for (int i = 0; i < kAbsMaxDn / 16; ++i) {
+      const int r = (tid >> 4) + 16 * i;
+      *(uint4*)(wsm + r * kAbsPitch + (tid & 15) * 16) = r < d_n ? st[i] : make_uint4(0, 0, 0, 0);
+    }
   }
   __syncthreads();
 
