@@ -341,7 +341,7 @@ def main():
     util = None
     dec_kernel = "decode_fp8_kernel" if cfg.kv_dtype == "fp8" else "decode_sf_kernel"
     tpath = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
-                         "decode_hs_b64_l8k_paged_counters.json")
+                         "decode_sf_b64_l8k_paged_counters.json")
     if os.path.exists(tpath):
         try:
             with open(tpath) as f:
