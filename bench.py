@@ -339,7 +339,7 @@ def main():
 
     traffic = None
     util = None
-    dec_kernel = "decode_fp8_kernel" if cfg.kv_dtype == "fp8" else "decode_sf_kernel"
+    dec_kernel = "decode_sf_kernel<true>" if cfg.kv_dtype == "fp8" else "decode_sf_kernel<false>"
     tpath = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
                          "decode_sf_b64_l8k_paged_counters.json")
     if os.path.exists(tpath):

@@ -1,25 +1,26 @@
-// Split-K MLA decode for gfx950, latent 512 + RoPE 64, two kernels.
+// Split-K MLA decode for gfx950, latent 512 + RoPE 64.
 //
 // Pages cited (title, section):
 //   [ARCH] "Model Architecture Driving Inference Systems: From MHA/GQA to
 //          DeepSeek MLA Matrix Absorption and Memory Minimalism"
+//   [MATH] "Multi-Head Latent Attention (MLA): Mathematical Foundations, ..."
+//          (section on high-throughput serving kernels: fp8 latent cache)
 //
 // Query rows are (query i, head h) pairs, row i*H + h.  The cache is walked
 // in 32-token sub-tiles, each staged once in LDS for all the workgroup's rows
-// ([ARCH] 3.1: every head scores the same raw latent).  Both kernels compute
+// ([ARCH] 3.1: every head scores the same raw latent).  The kernel computes
 // in fp16: the absorbed query arrives in fp16, and the staged cache rows are
 // converted exactly to fp16 in LDS (every bf16 value of magnitude 2^-17 ..
 // 65504 and every e4m3 value is an fp16 value), so scores against long
 // contexts with large cached values keep the query's 11-bit significand.
 //
-// decode_sf_kernel (bf16 cache): one workgroup = one split-K unit x 128 rows,
-// 8 waves, each owning 16 rows for both products (see the kernel).
-//
-// decode_fp8_kernel (fp8 e4m3 cache with per-token scales): one workgroup =
-// one split-K unit x 128 rows, every wave in both roles in turn (wave w
-// scores rows 16w.. with 11 k-slices in registers and 7 in LDS, then sums
-// latent columns 64w.. for all 128 rows); each staged sub-tile is first
-// converted exactly to fp16 in LDS, and the scales enter the scores and P.
+// decode_sf_kernel<F8>: one workgroup = one split-K unit x 128 rows, 8
+// waves, each owning 16 rows for both products (see the kernel).  bf16
+// cache: the sub-tiles land in a 4-slot ring and are converted in place,
+// each wave converting the rows it loaded.  fp8 e4m3 cache with per-token
+// fp32 scales ([MATH]): the raw rows of 4 sub-tiles are staged, and all 512
+// threads convert the next one into one of 2 fp16 slots; the scales multiply
+// the scores and ride in P for the value product.
 //
 // Operand layouts:
 //   16x16x32  A: lane l row l%16, k 8(l/16)..+7; B: column l%16, same k;
@@ -57,27 +58,7 @@ using namespace dec;
 
 constexpr int kSub = 32;                       // tokens per LDS sub-tile
 constexpr int kSubBytes = kSub * 576 * 2;      // 36864
-constexpr int kRing = 3;
-constexpr int kPPitch = 80;                    // bytes per row of P (32 bf16 + pad)
-constexpr int kPBytes = 128 * kPPitch;         // 10240
 constexpr int kF8Stage = 32 * 512 + 32 * 64 + 256;  // 18688: fp8 rows + scales
-
-// LDS map of the fp8 kernel: the ring stages raw e4m3 rows and per-token
-// scales, and one bf16 tile receives the exact conversion of the sub-tile in
-// use.
-struct LdsF8 {
-  // k-slices of Q (32 columns each) kept in registers; the rest live in LDS
-  static constexpr int kQReg = 11;
-  static constexpr int kQLds = 18 - kQReg;
-  static constexpr int kStage = kF8Stage;             // bytes per ring slot
-  static constexpr int kConv = kRing * kStage;        // the converted tile
-  static constexpr int kOffP = kConv + kSubBytes;
-  static constexpr int kOffAlpha = kOffP + kPBytes;
-  static constexpr int kOffL = kOffAlpha + 512;
-  static constexpr int kOffFlag = kOffL + 512;
-  static constexpr int kOffQ = kOffFlag + 128;
-  static constexpr int kBytes = kOffQ + kQLds * 8192;  // 161664
-};
 
 // Next 32-token sub-tile: second half of the tile, or the next tile.
 __device__ __forceinline__ void step_sub(int64_t& x, int& hh) {
@@ -215,308 +196,6 @@ __device__ __forceinline__ uint32_t off_qk(int lane) {
   return (uint32_t)(g1 * 1024 + 128 * (g ^ g1) + 16 * ((lane & 7) ^ (4 * fq)));
 }
 
-// Value B operand: the two transposed 8-byte reads rd = 0, 1.
-__device__ __forceinline__ uint32_t off_pv(int lane, int w, int rd) {
-  const int li = lane & 15, hf = lane >> 5;
-  const int ch = (lane >> 4) & 1, bq = (li & 3) >> 1;
-  const int rho_v = 4 * hf + (li >> 2);
-  return (uint32_t)(w * 4096 + rd * 1024 + 256 * ch + 128 * (bq ^ rd) +
-                    16 * (rho_v ^ (4 * (bq ^ ch))) + 8 * (li & 1));
-}
-
-// This lane's P write and P (A operand) read.
-__device__ __forceinline__ uint32_t off_pw(int lane, int w) {
-  const int g = lane >> 4, li = lane & 15;
-  return (uint32_t)((16 * w + li) * kPPitch + (g & 1) * 16 + (g >> 1) * 8);
-}
-__device__ __forceinline__ uint32_t off_pr(int lane) {
-  return (uint32_t)((lane & 31) * kPPitch + (lane >> 5) * 16);
-}
-
-// Q k-slices held in LDS: rows of 64 B (row 16w + lane%16, chunk lane/16),
-// 16-byte chunk c of row r stored at chunk c ^ ((r >> 1) & 3).
-__device__ __forceinline__ uint32_t off_ql(int lane, int w) {
-  const int g = lane >> 4, li = lane & 15;
-  return (uint32_t)(LdsF8::kOffQ + (16 * w + li) * 64 + 16 * (g ^ ((li >> 1) & 3)));
-}
-
-__global__ __launch_bounds__(512, 1) void decode_fp8_kernel(DecodeArgs a) {
-  using L = LdsF8;
-  __shared__ __attribute__((aligned(1024))) char smem[L::kBytes];
-
-  const int lane = threadIdx.x & 63;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int g = lane >> 4, li = lane & 15;    // 16x16 operand coordinates
-  const int hf = lane >> 5, n32 = lane & 31;  // 32x32 operand coordinates
-  const int R = a.q_len * a.heads;
-  const int rowg = blockIdx.y * 128;
-  const int qrow0 = rowg + 16 * w;            // rows this wave scores
-  const bool qk_active = qrow0 < R;
-  const int qi = qk_active ? qrow0 / a.heads : 0;
-  const int h0 = qk_active ? qrow0 % a.heads : 0;
-  const int u = blockIdx.x;
-  const int my_loads = w < 3 ? 3 : 2;  // direct loads per sub-tile
-
-  int64_t x0, x1;  // this unit's tiles
-  TileWin win;
-  if (a.batch <= 64) {
-    if (!unit_window_small(a, u, lane, x0, x1, win)) return;  // uniform across the workgroup
-  } else {
-    int64_t T, unused;
-    wave_tile_sums(a.seq_lens, a.batch, 0, T, unused);
-    T = uniform64(T);
-    x0 = unit_begin(u, T, a.num_splits);
-    x1 = unit_begin(u + 1, T, a.num_splits);
-    if (x0 >= x1) return;  // uniform across the workgroup
-    int b;
-    int64_t pb;
-    find_sequence(a.seq_lens, a.batch, x0, b, pb);
-    build_window(a, x0, x1, __builtin_amdgcn_readfirstlane(b), uniform64(pb), lane, win);
-  }
-
-  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_char*)smem;
-  char* pbuf = smem + L::kOffP;
-  float* alpha_buf = (float*)(smem + L::kOffAlpha);
-  float* lbuf = (float*)(smem + L::kOffL);
-  uint8_t* flags = (uint8_t*)(smem + L::kOffFlag);
-  // issue the direct loads of (tile x, half hh) into ring slot `sl`
-  auto issue = [&](const TileInfo& t, int hh, int sl, int lane_) {
-    const uint32_t dst = lds0 + (uint32_t)(sl * L::kStage);
-    issue_all_f8(plan_sub_f8(a, t, hh, dst, w, lane_), w);
-  };
-  const float sl2 = a.softmax_scale * kLog2e;
-
-  // ---- prologue: sub-tiles 0 and 1 of the unit (a unit has >= 1 tile = 2 subs)
-  const int64_t nsub = 2 * (x1 - x0);
-  int64_t cx = x0, px = x0;  // tile of the sub-tile in use / next to issue
-  int chh = 0, phh = 0;      // and its half
-  issue(tile_info(win, px), phh, 0, lane);
-  step_sub(px, phh);
-  issue(tile_info(win, px), phh, 1, lane);
-  step_sub(px, phh);
-
-  constexpr int kQReg = L::kQReg;
-  f16x8 q[kQReg];
-  f32x16 o[4][2];
-  float m_run = -INFINITY, l_run = 0.f;
-  bool new_seg = true;
-  int slot = 0;
-
-  for (int64_t y = 0; y < nsub; ++y) {
-    const int ln = fresh_lane();
-    const TileInfo ci = tile_info(win, cx);
-    if (new_seg) {
-      new_seg = false;
-      {  // unconditional (inactive waves read row 0) so q is dead between segments
-        const f16x8* qp = (const f16x8*)((const _Float16*)a.q_abs +
-                                            (((int64_t)ci.b * a.q_len + qi) * a.heads + h0 + li) * 576);
-#pragma unroll
-        for (int kk = 0; kk < kQReg; ++kk) q[kk] = qp[4 * kk + g];
-#pragma unroll
-        for (int kk = kQReg; kk < 18; ++kk)
-          *(f16x8*)(smem + off_ql(ln, w) + (kk - kQReg) * 8192) = qp[4 * kk + g];
-      }
-      wait_vm0();
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb) o[mb][0] = o[mb][1] = f32x16{};
-      m_run = -INFINITY;
-      l_run = 0.f;
-    }
-    // sub-tile y has landed (the only newer loads are sub-tile y+1's)
-    if (y + 1 < nsub)
-      wait_vm(my_loads);
-    else
-      wait_vm(0);
-    block_sync();  // visible to all; everyone also finished sub-tile y-1
-    // the loads of sub-tile y+2, into the slot every wave finished with
-    if (y + 2 < nsub) {
-      const int s2 = slot + 2 >= kRing ? slot + 2 - kRing : slot + 2;
-      if (px >= win.wx + win.wn)  // slide the window to start at the tile in use
-        build_window(a, cx, x1, win.b0, win.pb0, ln, win);
-      issue(tile_info(win, px), phh, s2, ln);
-      step_sub(px, phh);
-    }
-
-    const char* stage = smem + slot * L::kStage;
-    const bool has_tokens = 32 * chh < ci.rem;  // uniform: an empty second half does nothing
-    if (has_tokens) {  // every wave converts its share, then all may read the tile
-      int tid = (int)threadIdx.x;
-      asm volatile("" : "+v"(tid));  // recompute the addresses, do not keep them live
-      convert_f8(stage, smem + L::kConv, tid);
-      block_sync();
-    }
-    const char* tile = smem + L::kConv;
-    char* pb = pbuf;  // one P buffer: the barrier at the top of the next
-                      // sub-tile orders its reuse after every wave's reads
-    // visible tokens of this sub-tile: all up to the sequence end, or with
-    // the causal mask those up to the query's own position
-    int nv = ci.rem - 32 * chh - (a.causal ? a.q_len - 1 - qi : 0);
-    nv = nv < 0 ? 0 : (nv > kSub ? kSub : nv);
-    const bool scores = has_tokens && qk_active && nv > 0;  // uniform per wave
-    if (has_tokens) {
-      // ---------------- scores and softmax for this wave's 16 rows
-      f16x8 pw = f16x8{};
-      bool need = false;
-      float alpha = 1.f;
-      if (scores) {
-        f32x4 s[2] = {f32x4{}, f32x4{}};
-        constexpr int kPf = 2;
-        const int lq = fresh_lane();
-        const uint32_t o_qk = off_qk(lq), o_ql = off_ql(lq, w);
-        f16x8 ka[kPf + 1][2], qb[kPf + 1];
-        auto kload = [&](int kk) {
-          const int e = kk % (kPf + 1);
-#pragma unroll
-          for (int j = 0; j < 2; ++j)
-            ka[e][j] = *(const f16x8*)(tile + (uint32_t)((kk >> 1) * 4096 + 2048 * j + 512 * (kk & 1)) + o_qk);
-          if (kk >= kQReg) qb[e] = *(const f16x8*)(smem + o_ql + (kk - kQReg) * 8192);
-        };
-#pragma unroll
-        for (int kk = 0; kk < kPf; ++kk) kload(kk);
-#pragma unroll
-        for (int kk = 0; kk < 18; ++kk) {
-          if (kk + kPf < 18) kload(kk + kPf);
-          const int e = kk % (kPf + 1);
-          const f16x8 qk = kk < kQReg ? q[kk < kQReg ? kk : 0] : qb[e];
-          s[0] = mfma16h(ka[e][0], qk, s[0]);
-          s[1] = mfma16h(ka[e][1], qk, s[1]);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        mfma_settle(s[0]);
-        mfma_settle(s[1]);
-        // the tokens' dequantisation scales
-        const float* scl = (const float*)(stage + 18432);
-        const f32x4 sc[2] = {*(const f32x4*)(scl + 4 * (ln >> 4)), *(const f32x4*)(scl + 16 + 4 * (ln >> 4))};
-        s[0] *= sc[0];
-        s[1] *= sc[1];
-        if (nv < kSub) {  // mask the tokens past the visible end
-#pragma unroll
-          for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-              if (16 * j + 4 * (ln >> 4) + r >= nv) s[j][r] = -INFINITY;
-        }
-        // this lane's max over its 8 scores, in log2 units
-        const float lm = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
-                               fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3]))) * sl2;
-        // Rescale only when some score passes its row's running max by more
-        // than 2^8 (log2 units): the exponentials stay <= 256 and the final
-        // normalisation uses the same reference max for numerator and
-        // denominator.  Only then is the row max reduced across lanes.
-        need = __ballot(lm > m_run + 8.f) != 0;
-        if (need) {
-          float mt = fmaxf(lm, __shfl_xor(lm, 16, 64));
-          mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-          const float m_new = fmaxf(m_run, mt);
-          alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-          m_run = m_new;
-          l_run *= alpha;
-        }
-        // exponent arguments are <= 8; results under 2^-126 flush to zero
-        const float m_use = m_run == -INFINITY ? 0.f : m_run;
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float e = __builtin_amdgcn_exp2f(fmaf(s[j][r], sl2, -m_use));
-            l_run += e;
-            // fp8: the value rows in LDS are unscaled, so P carries the scale
-            pw[4 * j + r] = (_Float16)(e * sc[j][r]);
-          }
-      }
-      // P rows of this wave's heads (zeros when it has nothing to score)
-      {
-        const uint32_t o_pw = off_pw(fresh_lane(), w);
-        *(f16x4*)(pb + o_pw) = __builtin_shufflevector(pw, pw, 0, 1, 2, 3);
-        *(f16x4*)(pb + o_pw + 32) = __builtin_shufflevector(pw, pw, 4, 5, 6, 7);
-      }
-      // every wave publishes its factors (1 when unchanged): a rescale reads all rows
-      if ((ln >> 4) == 0) alpha_buf[16 * w + (ln & 15)] = alpha;
-      if (lane == 0) flags[w] = need ? 1 : 0;
-      block_sync();
-
-      // ---------------- rescale (rare), then O[:, 64w..] += P V
-      const uint64_t fl = *(const uint64_t*)flags;
-      if (fl != 0) {
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb) {
-          f32x16 a16;
-#pragma unroll
-          for (int r4 = 0; r4 < 4; ++r4) {
-            const f32x4 a4 = *(const f32x4*)(alpha_buf + mb * 32 + 8 * r4 + 4 * (ln >> 5));
-#pragma unroll
-            for (int i = 0; i < 4; ++i) a16[4 * r4 + i] = a4[i];
-          }
-          o[mb][0] *= a16;
-          o[mb][1] *= a16;
-          __builtin_amdgcn_sched_barrier(0);  // one block's factors live at a time
-        }
-      }
-      const int lv = fresh_lane();
-      const uint32_t o_pr = off_pr(lv), o_pv0 = off_pv(lv, w, 0), o_pv1 = off_pv(lv, w, 1);
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        f16x8 pa[4], vb[2];
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
-          pa[mb] = *(const f16x8*)(pb + o_pr + (uint32_t)(mb * 32 * kPPitch + ks * 32));
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-          const uint32_t cb = (uint32_t)(2048 * ks + 512 * nb);
-          vb[nb] = cath(lds_tr4h(tile, cb + o_pv0), lds_tr4h(tile, cb + o_pv1));
-        }
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-          for (int nb = 0; nb < 2; ++nb) o[mb][nb] = mfma32h(pa[mb], vb[nb], o[mb][nb]);
-      }
-    }
-
-
-    // ---- end of this unit's part of the sequence: write the partial
-    const bool last = y + 1 >= nsub || (chh == 1 && ci.rem <= kTile);
-    if (last) {
-      float l_tot = l_run + __shfl_xor(l_run, 16, 64);
-      l_tot += __shfl_xor(l_tot, 32, 64);
-      const int64_t sl = (int64_t)u + ci.b;
-      if ((ln >> 4) == 0) {
-        lbuf[16 * w + (ln & 15)] = l_tot;
-        if (qk_active)
-          a.lse_part[sl * R + qrow0 + (ln & 15)] =
-              l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
-      }
-      block_sync();
-      // fp16 partial rows of 1 KB; rows past R fall outside the resource
-      // and are dropped
-      const int rows_here = min(128, R - rowg);
-      const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(
-          (_Float16*)a.o_part + (sl * R + rowg) * 512, (uint32_t)rows_here * 1024u);
-      const uint32_t vo = (uint32_t)((4 * hf * 512 + 64 * w + n32) * 2);
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
-        f32x16 inv16;
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const f32x4 l4 = *(const f32x4*)(lbuf + mb * 32 + 8 * r4 + 4 * hf);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) inv16[4 * r4 + i] = l4[i] > 0.f ? 1.f / l4[i] : 0.f;
-        }
-        const f32x16 v0 = o[mb][0] * inv16, v1 = o[mb][1] * inv16;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const uint32_t so = (uint32_t)((mb * 32 + 8 * (r >> 2) + (r & 3)) * 1024);
-          buffer_store_f16(v0[r], rs, vo, so);
-          buffer_store_f16(v1[r], rs, vo + 64, so);
-        }
-      }
-      new_seg = true;
-    }
-    step_sub(cx, chh);
-    slot = slot + 1 >= kRing ? 0 : slot + 1;
-  }
-}
-
-
 // ---------------------------------------------------------------------------
 // bf16 cache, single-fill kernel.  One workgroup per split-K unit holds a
 // block of 128 query rows, so every 32-token sub-tile is loaded into LDS
@@ -549,6 +228,11 @@ constexpr int kSfSplit = 5;      // column groups [0, 5) loaded by waves 0-3, [5
 constexpr int kSfKPrefetch = 2;  // K operands read ahead of the score MFMAs
 constexpr int kSfBytes = kSfRing * kSubBytes;  // 147456
 static_assert(kSfBytes <= 163840, "LDS budget");
+// fp8: 2 converted sub-tiles, 4 staged raw sub-tiles, 2 x 32 token scales
+constexpr int kSf8Stage0 = 2 * kSubBytes;
+constexpr int kSf8Scale0 = kSf8Stage0 + 4 * kF8Stage;
+constexpr int kSf8Bytes = kSf8Scale0 + 256;  // 148736
+static_assert(kSf8Bytes <= 163840, "LDS budget");
 
 // Load cg (0-7 latent, 8 RoPE) of row group (w & 3).
 __device__ __forceinline__ void issue_cg(const DmaPlan& p, int w, int cg) {
@@ -585,8 +269,9 @@ __device__ __forceinline__ uint32_t vt_base(int lane, int rd, int par) {
   return (uint32_t)(rg * 1024 + 128 * (b ^ (rg & 1)) + 16 * (rho ^ (4 * ((b ^ par) & 1))) + 8 * (i & 1));
 }
 
+template <bool F8>
 __global__ __launch_bounds__(512, 1) void decode_sf_kernel(DecodeArgs a) {
-  __shared__ __attribute__((aligned(1024))) char smem[kSfBytes];
+  __shared__ __attribute__((aligned(1024))) char smem[F8 ? kSf8Bytes : kSfBytes];
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -613,7 +298,17 @@ __global__ __launch_bounds__(512, 1) void decode_sf_kernel(DecodeArgs a) {
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_char*)smem;
   const int64_t nsub = 2 * (x1 - x0);  // a unit has >= 1 tile = 2 sub-tiles
   const int cg0 = w < 4 ? 0 : kSfSplit, cg1 = w < 4 ? kSfSplit : 9;
-  const int n_share = cg1 - cg0;  // direct loads per sub-tile of this wave
+  // direct loads per sub-tile of this wave (fp8: loads k = w, w + 8, w + 16 of 19)
+  const int n_share = F8 ? (w < 3 ? 3 : 2) : cg1 - cg0;
+  // bf16: ring of 4 sub-tiles converted in place.  fp8: the raw rows of 4
+  // sub-tiles are staged (issued 4 ahead), 2 converted sub-tiles and their
+  // token scales are read by the products.
+  auto tile_of = [&](int64_t z) -> char* {
+    return smem + (F8 ? (int)(z & 1) : (int)(z & 3)) * kSubBytes;
+  };
+  auto stage_of = [&](int64_t z) -> char* { return smem + kSf8Stage0 + (int)(z & 3) * kF8Stage; };
+  auto scales_of = [&](int64_t z) -> float* { return (float*)(smem + kSf8Scale0 + (int)(z & 1) * 128); };
+  constexpr int kAhead = F8 ? 4 : 3;  // sub-tiles issued ahead of the one in use
 
   // rows of this wave
   const int qrow0 = blockIdx.y * kSfRows + 16 * w;
@@ -625,17 +320,41 @@ __global__ __launch_bounds__(512, 1) void decode_sf_kernel(DecodeArgs a) {
   // next sub-tile to load: tile px, half phh, ring index pz
   int64_t px = x0, pz = 0;
   int phh = 0;
-  auto plan_next = [&](int ln) {
+  auto slide = [&](int ln) {
     if (px >= win.wx + win.wn)  // slide the window to start at the tile in use
       build_window(a, px - 2, x1, win.b0, win.pb0, ln, win);
+  };
+  auto plan_next = [&](int ln) {
+    slide(ln);
     const DmaPlan plan = plan_sub(a, tile_info(win, px), phh, lds0 + (uint32_t)((pz & 3) * kSubBytes), w, ln);
+    step_sub(px, phh);
+    ++pz;
+    return plan;
+  };
+  auto plan_next_f8 = [&](int ln) {
+    slide(ln);
+    const F8Plan plan = plan_sub_f8(a, tile_info(win, px), phh,
+                                    lds0 + (uint32_t)(kSf8Stage0 + (pz & 3) * kF8Stage), w, ln);
     step_sub(px, phh);
     ++pz;
     return plan;
   };
   // this wave's loaded chunks of sub-tile z, bf16 -> fp16 in place, once
   // they have landed (its loads of later sub-tiles may stay in flight)
+  // fp8: this thread's chunks of sub-tile z (staged by all waves, whose
+  // loads of z landed before the last barrier), e4m3 -> fp16, and its token
+  // scales (wave 4)
+  auto convert_sub_f8 = [&](int64_t z, int ln) {
+    int tid = (int)threadIdx.x;
+    asm volatile("" : "+v"(tid));  // recompute the addresses, do not keep them live
+    convert_f8(stage_of(z), tile_of(z), tid);
+    if (w == 4 && ln < 32) scales_of(z)[ln] = ((const float*)(stage_of(z) + 18432))[ln];
+  };
   auto convert_sub = [&](int64_t z, int ln) {
+    if (F8) {
+      convert_sub_f8(z, ln);
+      return;
+    }
     wait_vm((int)(n_share * (pz - 1 - z)));
     char* base = smem + (int)(z & 3) * kSubBytes + (w & 3) * 1024 + 16 * ln;
     uint4 c[kSfSplit];
@@ -664,13 +383,19 @@ __global__ __launch_bounds__(512, 1) void decode_sf_kernel(DecodeArgs a) {
     for (int kk = 0; kk < 18; ++kk) asm volatile("" ::"v"(q[kk]));
   };
 
-  // ---- prologue: sub-tiles 0..2 in flight, this wave's query, sub-tile 0 converted
-  for (int z = 0; z < 3 && z < nsub; ++z) {
-    const DmaPlan plan = plan_next(lane);
-    for (int cg = cg0; cg < cg1; ++cg) issue_cg(plan, w, cg);
+  // ---- prologue: the first sub-tiles in flight, this wave's query, sub-tile
+  // 0 converted (fp8: and sub-tile 1 landed)
+  for (int z = 0; z < kAhead && z < nsub; ++z) {
+    if (F8) {
+      issue_all_f8(plan_next_f8(lane), w);
+    } else {
+      const DmaPlan plan = plan_next(lane);
+      for (int cg = cg0; cg < cg1; ++cg) issue_cg(plan, w, cg);
+    }
   }
   load_q(tile_info(win, x0).b, lane);
   wait_vm0();
+  if (F8) block_sync();  // every wave's rows of the first sub-tiles in LDS
   convert_sub(0, lane);
   block_sync();
 
@@ -696,17 +421,24 @@ __global__ __launch_bounds__(512, 1) void decode_sf_kernel(DecodeArgs a) {
       m_run = -INFINITY;
       l_run = 0.f;
     }
-    const char* tile = smem + (int)(s & 3) * kSubBytes;
+    const char* tile = tile_of(s);
     // visible tokens of this sub-tile: all up to the sequence end, or with
     // the causal mask those up to the query's own position
     int nv = ci.rem - 32 * chh - (a.causal ? a.q_len - 1 - qi : 0);
     nv = nv < 0 ? 0 : (nv > kSub ? kSub : nv);
     const bool work = active && nv > 0;  // uniform per wave
     const bool last = s + 1 >= nsub || (chh == 1 && ci.rem <= kTile);
-    const bool more = s + 3 < nsub;
+    const bool more = s + kAhead < nsub;
     DmaPlan plan{};
-    if (more) plan = plan_next(ln);
-    int issued = cg0;  // column groups of sub-tile s+3 issued so far
+    F8Plan plan8{};
+    if (more) {
+      if (F8)
+        plan8 = plan_next_f8(ln);
+      else
+        plan = plan_next(ln);
+    }
+    int issued = cg0;  // column groups of sub-tile s+3 issued so far (bf16)
+    bool issued8 = false;
 
     if (work) {
       // ------------------------------------------------ scores and softmax
@@ -734,6 +466,13 @@ __global__ __launch_bounds__(512, 1) void decode_sf_kernel(DecodeArgs a) {
         asm volatile("s_nop 15\n\ts_nop 7" : "+v"(sc[0]), "+v"(sc[1]));
       }
       ln = fresh_lane();
+      f32x4 tsc[2];  // fp8: the tokens' dequantisation scales
+      if (F8) {
+        tsc[0] = *(const f32x4*)(scales_of(s) + 4 * (ln >> 4));
+        tsc[1] = *(const f32x4*)(scales_of(s) + 16 + 4 * (ln >> 4));
+        sc[0] *= tsc[0];
+        sc[1] *= tsc[1];
+      }
       if (nv < kSub) {  // mask the tokens past the visible end
 #pragma unroll
         for (int jt = 0; jt < 2; ++jt)
@@ -765,7 +504,8 @@ __global__ __launch_bounds__(512, 1) void decode_sf_kernel(DecodeArgs a) {
         for (int r = 0; r < 4; ++r) {
           const float e = __builtin_amdgcn_exp2f(fmaf(sc[jt][r], sl2, -m_use));
           l_run += e;
-          p[4 * jt + r] = (_Float16)e;
+          // fp8: the value rows in LDS are unscaled, so P carries the scale
+          p[4 * jt + r] = (_Float16)(F8 ? e * tsc[jt][r] : e);
         }
 
       // ------------------------------------------------ O^T += V^T P^T
@@ -783,15 +523,27 @@ __global__ __launch_bounds__(512, 1) void decode_sf_kernel(DecodeArgs a) {
         const f16x8 vnn = nb + 2 < 32 ? vload(nb + 2) : vn;
         // this sub-tile's share of the loads of sub-tile s+3 goes out between
         // the MFMAs, so that the issue stalls overlap the matrix core's work
-        if ((nb & 3) == 3 && more && issued < cg1) issue_cg(plan, w, issued++);
+        if (F8) {
+          if (nb == 3 && more) {
+            issue_all_f8(plan8, w);
+            issued8 = true;
+          }
+        } else if ((nb & 3) == 3 && more && issued < cg1) {
+          issue_cg(plan, w, issued++);
+        }
         o[nb] = mfma16h(va, p, o[nb]);
         __builtin_amdgcn_sched_barrier(0);
         va = vn;
         vn = vnn;
       }
     }
-    if (more)
-      for (; issued < cg1; ++issued) issue_cg(plan, w, issued);  // the rest (all, without a value sum)
+    if (more) {  // the rest (all, without a value sum)
+      if (F8) {
+        if (!issued8) issue_all_f8(plan8, w);
+      } else {
+        for (; issued < cg1; ++issued) issue_cg(plan, w, issued);
+      }
+    }
 
     if (last) {  // end of this unit's part of the sequence: write the partial
       float l_tot = l_run + __shfl_xor(l_run, 16, 64);
@@ -820,6 +572,9 @@ __global__ __launch_bounds__(512, 1) void decode_sf_kernel(DecodeArgs a) {
     }
     // this wave's chunks of the next sub-tile, once they have landed
     if (w < 4 && s + 1 < nsub) convert_sub(s + 1, fresh_lane());
+    // fp8: this wave's rows of sub-tile s+2 landed, for its conversion in
+    // the next pass (the loads of s+3 and s+4 may stay in flight)
+    if (F8 && s + 2 < nsub) wait_vm((int)(n_share * (pz - 1 - (s + 2))));
     step_sub(cx, chh);
     block_sync();  // sub-tile s+1 complete for everyone; slot of s free
   }
@@ -838,11 +593,11 @@ bool mfma_decode_supports(const mla_dims_t& d, int64_t row_stride, const void* l
 hipError_t launch_decode_mfma(const mla_dims_t& d, const DecodeArgs& a, hipStream_t s) {
   const int R = d.q_len * d.heads;
   if (d.kv_dtype == MLA_FP8_E4M3) {
-    dim3 grid((unsigned)a.num_splits, (unsigned)((R + 127) / 128));
-    hipLaunchKernelGGL(decode_fp8_kernel, grid, dim3(512), 0, s, a);
+    dim3 grid((unsigned)a.num_splits, (unsigned)((R + kSfRows - 1) / kSfRows));
+    hipLaunchKernelGGL(decode_sf_kernel<true>, grid, dim3(512), 0, s, a);
   } else {
     dim3 grid((unsigned)a.num_splits, (unsigned)((R + kSfRows - 1) / kSfRows));
-    hipLaunchKernelGGL(decode_sf_kernel, grid, dim3(512), 0, s, a);
+    hipLaunchKernelGGL(decode_sf_kernel<false>, grid, dim3(512), 0, s, a);
   }
   return hipGetLastError();
 }
