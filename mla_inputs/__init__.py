@@ -7,7 +7,7 @@ the attention arithmetic: no RoPE, no projection, no softmax.  Both the CPU
 oracle and the GPU path consume what it produces.
 """
 
-from .configs import BLOCK_TOKENS, CONFIGS, HEADLINE, MLAConfig, scaled
+from .configs import BLOCK_TOKENS, CONFIGS, HEADLINE, PREFILL_CONFIGS, MLAConfig, scaled
 from .generate import AppendInputs, MLAInputs, Pool
 
 __all__ = [
@@ -17,6 +17,7 @@ __all__ = [
     "HEADLINE",
     "MLAConfig",
     "MLAInputs",
+    "PREFILL_CONFIGS",
     "Pool",
     "scaled",
 ]

@@ -114,3 +114,13 @@ CONFIGS = {
 }
 
 HEADLINE = "dsv3_b64_l8k_paged"
+
+# Prefill (MHA form): every cached token of a sequence is also a query token
+# of its prompt, under the causal mask.  Kept apart from the decode
+# workloads: it runs the prefill calls, not the decode step.
+PREFILL_CONFIGS = {
+    # batch 4 prompts of 4096 tokens, paged 64-token blocks.
+    "prefill_b4_s4k": MLAConfig(
+        name="prefill_b4_s4k", batch=4, q_len=4096, seq_len=4096, paged=True,
+        causal=True, query_in_cache=True, seed=20261210, **_DSV3),
+}

@@ -13,6 +13,7 @@ from .mla_oracle import (
     kv_cache_bytes_per_token,
     mla_absorbed,
     mla_decode,
+    mla_expand,
     rms_norm,
     rope_interleaved,
     stored_to_f64,
@@ -26,6 +27,7 @@ __all__ = [
     "kv_cache_bytes_per_token",
     "mla_absorbed",
     "mla_decode",
+    "mla_expand",
     "rms_norm",
     "rope_interleaved",
     "stored_to_f64",

@@ -26,6 +26,9 @@ Readings where the pages leave a step open:
     t <= len - q_len + i (bottom-right aligned).
   * A row that sees no token gets o = 0 and lse = -inf.
   * fp8 rows are OCP E4M3 codes times one fp32 scale per token.
+  * Prefill in MHA form (``mla_expand`` then ``mla_decode``): the prompt's
+    q_len tokens are the last q_len of the sequence's cached tokens and see
+    them causally, as any multi-token query does.
   * The cache-append producer (``kv_append``): RMSNorm with eps as given by
     the caller (the module on [MATH] uses the framework default); the new
     token's key is rotated at its own position.
@@ -189,6 +192,28 @@ def mla_decode(inp, rows: Optional[Iterable] = None):
                 o[b, i, h] = p @ values[:n]
                 lse[b, i, h] = m + np.log(z)
     return {"o": o, "lse": lse}
+
+
+def mla_expand(inp, b: int):
+    """Per-head content keys and values of sequence b's cached latents, the
+    first step of the MHA form used for prefill ("DeepSeek's attention
+    evolution - [MLA]" 2.5; [ARCH] 2.3 content key W^UK c, 3.2 value W^UV c):
+
+      k_nope[t, h, :] = W_UK[h] c_t      (d_nope)
+      v[t, h, :]      = W_UV[h] c_t      (d_v)
+
+    Returns (k_nope [len_b, H, d_nope], v [len_b, H, d_v]) float64.  The
+    attention that follows is ``mla_decode`` itself: with q_len prompt tokens
+    and ``causal`` it scores exactly these keys and values.
+    """
+    cfg = inp.cfg
+    dc = cfg.d_latent
+    c_kv = cache_f64(inp, b)[:, :dc]
+    w_uk = stored_to_f64(inp.w_uk, cfg.q_dtype)
+    w_uv = stored_to_f64(inp.w_uv, cfg.q_dtype)
+    k_nope = np.einsum("hdc,tc->thd", w_uk, c_kv)
+    v = np.einsum("hdc,tc->thd", w_uv, c_kv)
+    return k_nope, v
 
 
 def mla_absorbed(inp, rows: Optional[Iterable] = None):

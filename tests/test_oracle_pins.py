@@ -18,7 +18,7 @@ import torch
 from mla_inputs import CONFIGS, MLAInputs, scaled
 from mla_inputs.generate import bf16_bits_from_f32
 from oracle import (bf16_to_f64, e4m3_to_f64, kv_cache_bytes_per_token, mla_absorbed,
-                    mla_decode, rope_interleaved)
+                    mla_decode, mla_expand, rope_interleaved)
 from tests._fake import ArrayInputs, random_arrays
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -193,6 +193,54 @@ def test_oracle_matches_torch_sdpa(Lq, causal):
                 mask = t <= (L - Lq + i)
             o = torch.nn.functional.scaled_dot_product_attention(
                 Q[None], K[None], V[None], attn_mask=mask[None], scale=1.0 / math.sqrt(12 + 8))
+            np.testing.assert_allclose(ref["o"][b, :, h], o[0].numpy(), rtol=1e-11, atol=1e-13)
+
+
+# ------------------------------------------------ prefill in MHA form
+
+
+def test_expand_matches_brute_force():
+    """k_nope[t, h, j] = sum_c W_UK[h][j][c] c_t[c] and the same with W_UV,
+    element by element with scalar loops."""
+    arr = _arrays(11, B=2, lens=(5, 3))
+    inp = ArrayInputs(**arr)
+    d = DIMS
+    for b in range(2):
+        k, v = mla_expand(inp, b)
+        assert k.shape == (len(inp.caches[b]), d["H"], d["d_n"])
+        assert v.shape == (len(inp.caches[b]), d["H"], d["d_v"])
+        c = inp.caches[b]
+        for t in range(len(c)):
+            for h in range(d["H"]):
+                for j in range(d["d_n"]):
+                    ref = sum(float(inp.w_uk[h, j, cc]) * float(c[t, cc]) for cc in range(d["d_c"]))
+                    assert abs(k[t, h, j] - ref) < 1e-12
+                for j in range(d["d_v"]):
+                    ref = sum(float(inp.w_uv[h, j, cc]) * float(c[t, cc]) for cc in range(d["d_c"]))
+                    assert abs(v[t, h, j] - ref) < 1e-12
+
+
+def test_prefill_is_causal_self_attention():
+    """A prompt of q_len = len tokens that are all cached: the oracle's output
+    equals torch's float64 causal attention (is_causal, no explicit mask) over
+    keys [W_UK c ; k_rope] and values W_UV c built from the expand step."""
+    L = 9
+    arr = _arrays(12, B=2, Lq=L, lens=(L, L))
+    arr["positions"] = np.tile(np.arange(L), (2, 1))
+    inp = ArrayInputs(**arr, causal=True)
+    ref = mla_decode(inp)
+    d = DIMS
+    for b in range(2):
+        k, v = mla_expand(inp, b)
+        kr = inp.caches[b][:, d["d_c"]:].astype(np.float64)
+        for h in range(d["H"]):
+            K = torch.from_numpy(np.concatenate([k[:, h], kr], axis=1))
+            V = torch.from_numpy(v[:, h])
+            qr = np.stack([rope_interleaved(inp.q_rope[b, i, h], inp.positions[b, i], 10000.0)
+                           for i in range(L)])
+            Q = torch.from_numpy(np.concatenate([inp.q_nope[b, :, h].astype(np.float64), qr], axis=1))
+            o = torch.nn.functional.scaled_dot_product_attention(
+                Q[None], K[None], V[None], is_causal=True, scale=1.0 / math.sqrt(12 + 8))
             np.testing.assert_allclose(ref["o"][b, :, h], o[0].numpy(), rtol=1e-11, atol=1e-13)
 
 
