@@ -305,6 +305,67 @@ int mla_kv_append_noalloc(const mla_append_dims_t* dims, const void* h, const vo
                           void* latent_cache, void* rope_cache, int64_t kv_row_stride,
                           float* kv_scale, void* stream);
 
+/*
+ * ---- Prefill in MHA form ([ARCH] FAQ on prefill; "DeepSeek's attention
+ * evolution - [MLA]" 2.5).  In prefill every prompt token is a query, so
+ * absorbing W_UK into the queries would score 512-wide latents instead of
+ * 128-wide keys (~4x the attention flops); the latent is expanded into
+ * per-head keys and values once instead, and ordinary causal attention runs
+ * over them.  Both calls are built for bf16 (q_dtype = kv_dtype =
+ * MLA_BF16), d_nope = d_v = 128, d_rope = 64, d_latent = 512, kv_row_stride
+ * a multiple of 8 up to 65536, max_seq_len <= 262144 and
+ * batch * ceil(max_seq_len / 128) <= 65535; anything else returns
+ * MLA_ERR_UNSUPPORTED.
+ */
+
+/*
+ * mla_prefill_expand -- per-head keys and values of the cached latents.
+ *
+ *   k_nope[b, t, h, :] = W_UK,h c_t     ([ARCH] 2.3: content key W^UK c)
+ *   v[b, t, h, :]      = W_UV,h c_t     ([ARCH] 3.2: value W^UV c)
+ * for every t < seq_lens[b] (fp32 accumulate, bf16 result); rows
+ * t >= seq_lens[b] are not written.
+ *
+ *   latent_cache, kv_row_stride, seq_lens, block_table, max_blocks_per_seq,
+ *   block_size, max_seq_len: the cache rows, addressed as in mla_decode_attn
+ *   w_uk     [H, d_nope, d_latent] bf16
+ *   w_uv     [H, d_v, d_latent]    bf16
+ *   k_nope   [B, max_seq_len, H, d_nope] bf16, output
+ *   v        [B, max_seq_len, H, d_v]    bf16, output
+ */
+int mla_prefill_expand(const mla_dims_t* dims, const void* latent_cache, int64_t kv_row_stride,
+                       const int32_t* seq_lens, const int32_t* block_table,
+                       int32_t max_blocks_per_seq, int32_t block_size, int32_t max_seq_len,
+                       const void* w_uk, const void* w_uv, void* k_nope, void* v, void* stream);
+
+/*
+ * mla_prefill_attn -- attention of the prompt over the expanded keys.
+ *
+ * Query i of sequence b (the prompt's Lq tokens are the last Lq of its
+ * seq_lens[b] cached tokens) scores every visible token t:
+ *   s_t = ([q_nope ; RoPE(q_rope, pos)] . [k_nope_t ; k_rope_t]) * softmax_scale
+ * ([ARCH] 2.3: decoupled query and key; 3.1: score), with t <= seq_lens[b]
+ * - Lq + i when causal (else every cached token), and
+ *   o = softmax(s) . v,   lse = log sum_t exp(s_t).
+ * A query that sees no token gets o = 0, lse = -inf.
+ *
+ *   q_nope     [B, Lq, H, d_nope] bf16
+ *   q_rope     [B, Lq, H, d_rope] bf16, before rotation (as mla_absorb_q)
+ *   positions  [B, Lq] int32
+ *   rope_base  e.g. 10000
+ *   k_nope, v  outputs of mla_prefill_expand for the same cache
+ *   rope_cache the post-RoPE keys, rows addressed as in mla_decode_attn
+ *   causal     0 or 1
+ *   o          [B, Lq, H, d_v] bf16, output
+ *   lse        [B, Lq, H] fp32 natural-log LSE, output; may be NULL
+ */
+int mla_prefill_attn(const mla_dims_t* dims, const void* q_nope, const void* q_rope,
+                     const int32_t* positions, float rope_base, const void* k_nope,
+                     const void* v, const void* rope_cache, int64_t kv_row_stride,
+                     const int32_t* seq_lens, const int32_t* block_table,
+                     int32_t max_blocks_per_seq, int32_t block_size, int32_t max_seq_len,
+                     int32_t causal, float softmax_scale, void* o, float* lse, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

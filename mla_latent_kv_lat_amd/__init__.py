@@ -10,13 +10,14 @@ from .binding import (BF16, F32, FLAG_GENERIC, FP8_E4M3, TILE_TOKENS, MLAAppendD
                       MLAError, append_dims, dims, mla_kv_append, mla_kv_append_noalloc,
                       mla_kv_append_workspace_bytes,
                       mla_absorb_q, mla_combine, mla_combine_out_proj, mla_decode_attn, mla_num_splits_hint,
-                      mla_out_proj, mla_split_plan, mla_workspace_bytes,
-                      mla_workspace_elems)
+                      mla_out_proj, mla_prefill_attn, mla_prefill_expand, mla_split_plan,
+                      mla_workspace_bytes, mla_workspace_elems)
 from .step import DecodeStep
 
 __all__ = [
     "BF16", "F32", "FLAG_GENERIC", "FP8_E4M3", "TILE_TOKENS", "MLAAppendDims", "MLADims", "MLAError",
     "append_dims", "dims", "mla_kv_append", "mla_kv_append_noalloc", "mla_kv_append_workspace_bytes",
     "mla_absorb_q", "mla_combine", "mla_combine_out_proj", "mla_decode_attn", "mla_num_splits_hint", "mla_out_proj",
-    "mla_split_plan", "mla_workspace_bytes", "mla_workspace_elems", "DecodeStep",
+    "mla_prefill_attn", "mla_prefill_expand", "mla_split_plan", "mla_workspace_bytes",
+    "mla_workspace_elems", "DecodeStep",
 ]

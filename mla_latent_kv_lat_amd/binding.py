@@ -70,6 +70,9 @@ def _load():
                           I64, VP, VP, VP],
         "mla_kv_append_noalloc": [ctypes.POINTER(MLAAppendDims), VP, VP, VP, VP, VP, F, F, VP, VP,
                                   VP, I64, VP, VP],
+        "mla_prefill_expand": [P, VP, I64, VP, VP, I32, I32, I32, VP, VP, VP, VP, VP],
+        "mla_prefill_attn": [P, VP, VP, VP, F, VP, VP, VP, I64, VP, VP, I32, I32, I32, I32, F, VP,
+                             VP, VP],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -215,3 +218,25 @@ def mla_kv_append_noalloc(d: MLAAppendDims, h, w_dkv, kv_norm_w, w_kr, positions
                                       _ptr(cache_rows), _ptr(latent_cache), _ptr(rope_cache),
                                       int(kv_row_stride), _ptr(kv_scale), _stream(stream)),
            "mla_kv_append_noalloc")
+
+
+def mla_prefill_expand(d: MLADims, latent_cache, kv_row_stride, seq_lens, block_table,
+                       max_blocks_per_seq, block_size, max_seq_len, w_uk, w_uv, k_nope, v,
+                       stream=None):
+    _check(_lib.mla_prefill_expand(ctypes.byref(d), _ptr(latent_cache), int(kv_row_stride),
+                                   _ptr(seq_lens), _ptr(block_table), int(max_blocks_per_seq),
+                                   int(block_size), int(max_seq_len), _ptr(w_uk), _ptr(w_uv),
+                                   _ptr(k_nope), _ptr(v), _stream(stream)),
+           "mla_prefill_expand")
+
+
+def mla_prefill_attn(d: MLADims, q_nope, q_rope, positions, rope_base, k_nope, v, rope_cache,
+                     kv_row_stride, seq_lens, block_table, max_blocks_per_seq, block_size,
+                     max_seq_len, causal, softmax_scale, o, lse=None, stream=None):
+    _check(_lib.mla_prefill_attn(ctypes.byref(d), _ptr(q_nope), _ptr(q_rope), _ptr(positions),
+                                 float(rope_base), _ptr(k_nope), _ptr(v), _ptr(rope_cache),
+                                 int(kv_row_stride), _ptr(seq_lens), _ptr(block_table),
+                                 int(max_blocks_per_seq), int(block_size), int(max_seq_len),
+                                 int(causal), float(softmax_scale), _ptr(o), _ptr(lse),
+                                 _stream(stream)),
+           "mla_prefill_attn")

@@ -149,5 +149,37 @@ __device__ __forceinline__ int fresh_lane() {
   return l;
 }
 
+// ---- operand addresses in the sub-tile LDS layout (1 KB blocks of 8 rows x
+// 8 16-byte chunks; block (cg, rg) at (cg*4 + rg) KB; row rho / chunk kappa
+// of a block at entry 8*(kappa ^ (rg&1)) + (rho ^ 4*((kappa ^ kappa>>1)&1)))
+
+// Per-lane LDS byte offsets of the operand reads, computed where they are
+// used from fresh_lane().
+// Score A operand inside a sub-tile.  Sub-tile blocks of 8 rows x 8 chunks:
+// row rho / chunk kappa of block (cg, rg) at entry
+// 8*(kappa ^ (rg&1)) + (rho ^ 4*((kappa ^ kappa>>1)&1)).
+__device__ __forceinline__ uint32_t off_qk(int lane) {
+  const int g = lane >> 4, li = lane & 15;
+  const int g1 = (li >> 3) & 1;
+  const int fq = (g ^ (g >> 1)) & 1;
+  return (uint32_t)(g1 * 1024 + 128 * (g ^ g1) + 16 * ((lane & 7) ^ (4 * fq)));
+}
+
+
+// Lane part of the V^T operand address (16x16x32 A: lane l holds latent
+// column 16 nb + l%16, tokens 4(l/16)..+3 for rd = 0, 16 + 4(l/16)..+3 for
+// rd = 1).  Lane l names token 16 rd + 4g + i/4 and columns
+// 16 nb + 4(i%4)..+3 (g = l/16, i = l%16); in the sub-tile layout that
+// address is this base (which depends on nb only through its parity) plus
+// (nb/4) * 4096 + (nb%4) * 256.  The reads are free of bank conflicts.
+__device__ __forceinline__ uint32_t vt_base(int lane, int rd, int par) {
+  const int g = lane >> 4, i = lane & 15;
+  const int rg = 2 * rd + (g >> 1);
+  const int rho = 4 * (g & 1) + (i >> 2);
+  const int b = (i >> 1) & 1;
+  return (uint32_t)(rg * 1024 + 128 * (b ^ (rg & 1)) + 16 * (rho ^ (4 * ((b ^ par) & 1))) + 8 * (i & 1));
+}
+
+
 }  // namespace dec
 }  // namespace mla

@@ -27,6 +27,30 @@ struct DecodeArgs {
   float* lse_part;
 };
 
+// MHA-form prefill (bf16, d_nope = d_v = 128, d_rope = 64, d_latent = 512).
+struct PrefillArgs {
+  const void* latent;       // cache rows, as for decode
+  const void* rope;
+  int64_t row_stride;       // elements
+  const int32_t* seq_lens;
+  const int32_t* block_table;
+  int mbps, max_seq_len;
+  int batch, q_len, heads;
+  int causal;
+  float softmax_scale;
+  const uint16_t* w_uk;     // [H, 128, 512]
+  const uint16_t* w_uv;     // [H, 128, 512]
+  void* k_nope;             // [B, max_seq_len, H, 128]
+  void* v;                  // [B, max_seq_len, H, 128]
+  const void* q_nope;       // [B, Lq, H, 128]
+  const void* q_rope;       // [B, Lq, H, 64], before rotation
+  const int32_t* positions; // [B, Lq]
+  float rope_base;
+  void* o;                  // [B, Lq, H, 128]
+  float* lse;               // [B, Lq, H] or nullptr
+  int ntile;                // set by the expand launcher
+};
+
 hipError_t launch_absorb_generic(const mla_dims_t& d, const void* q_nope, const void* q_rope,
                                  const int32_t* positions, float rope_base, const void* w_uk,
                                  void* q_abs, hipStream_t s);
@@ -48,6 +72,9 @@ bool mfma_decode_supports(const mla_dims_t& d, int64_t row_stride, const void* l
 hipError_t launch_decode_mfma(const mla_dims_t& d, const DecodeArgs& a, hipStream_t s);
 bool mfma_out_proj_supports(const mla_dims_t& d);
 bool combine_proj_supports(const mla_dims_t& d);
+bool prefill_supports(const mla_dims_t& d, int64_t row_stride, int max_seq_len);
+hipError_t launch_prefill_expand(const mla_dims_t& d, const PrefillArgs& a, hipStream_t s);
+hipError_t launch_prefill_attn(const mla_dims_t& d, const PrefillArgs& a, hipStream_t s);
 hipError_t launch_combine_proj(const mla_dims_t& d, int num_splits, const int32_t* seq_lens,
                                const void* o_part, const float* lse_part, const void* w_uv,
                                void* o, float* lse_out, void* o_lat, hipStream_t s);

@@ -34,6 +34,19 @@ bool use_mfma(const mla_dims_t* d) { return !(d->flags & MLA_FLAG_GENERIC); }
 
 int launched(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_HIP; }
 
+int check_cache_args(const mla_dims_t* dims, int64_t kv_row_stride, const int32_t* seq_lens,
+                     const int32_t* block_table, int32_t max_blocks_per_seq, int32_t block_size,
+                     int32_t max_seq_len) {
+  if (!seq_lens) return MLA_ERR_INVALID_ARG;
+  if (kv_row_stride < dims->d_latent || kv_row_stride < dims->d_rope) return MLA_ERR_INVALID_ARG;
+  if (max_seq_len < 1) return MLA_ERR_INVALID_ARG;
+  if (block_table) {
+    if (block_size != MLA_TILE_TOKENS) return MLA_ERR_INVALID_ARG;
+    if ((int64_t)max_blocks_per_seq * MLA_TILE_TOKENS < max_seq_len) return MLA_ERR_INVALID_ARG;
+  }
+  return MLA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -238,6 +251,88 @@ int mla_split_plan(int32_t batch, const int32_t* seq_lens_host, int32_t num_spli
     pb += tb;
   }
   return MLA_OK;
+}
+
+
+// ------------------------------------------------------------- prefill
+
+
+int mla_prefill_expand(const mla_dims_t* dims, const void* latent_cache, int64_t kv_row_stride,
+                       const int32_t* seq_lens, const int32_t* block_table,
+                       int32_t max_blocks_per_seq, int32_t block_size, int32_t max_seq_len,
+                       const void* w_uk, const void* w_uv, void* k_nope, void* v, void* stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (dims->batch == 0) return MLA_OK;
+  if (!latent_cache || !w_uk || !w_uv || !k_nope || !v) return MLA_ERR_INVALID_ARG;
+  st = check_cache_args(dims, kv_row_stride, seq_lens, block_table, max_blocks_per_seq, block_size,
+                        max_seq_len);
+  if (st) return st;
+  if (!aligned16(latent_cache) || !aligned16(w_uk) || !aligned16(w_uv) || !aligned16(k_nope) ||
+      !aligned16(v))
+    return MLA_ERR_INVALID_ARG;
+  if (!prefill_supports(*dims, kv_row_stride, max_seq_len)) return MLA_ERR_UNSUPPORTED;
+  PrefillArgs a{};
+  a.latent = latent_cache;
+  a.row_stride = kv_row_stride;
+  a.seq_lens = seq_lens;
+  a.block_table = block_table;
+  a.mbps = max_blocks_per_seq;
+  a.max_seq_len = max_seq_len;
+  a.batch = dims->batch;
+  a.q_len = dims->q_len;
+  a.heads = dims->heads;
+  a.w_uk = (const uint16_t*)w_uk;
+  a.w_uv = (const uint16_t*)w_uv;
+  a.k_nope = k_nope;
+  a.v = v;
+  (void)hipGetLastError();
+  return launched(launch_prefill_expand(*dims, a, (hipStream_t)stream));
+}
+
+int mla_prefill_attn(const mla_dims_t* dims, const void* q_nope, const void* q_rope,
+                     const int32_t* positions, float rope_base, const void* k_nope,
+                     const void* v, const void* rope_cache, int64_t kv_row_stride,
+                     const int32_t* seq_lens, const int32_t* block_table,
+                     int32_t max_blocks_per_seq, int32_t block_size, int32_t max_seq_len,
+                     int32_t causal, float softmax_scale, void* o, float* lse, void* stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (dims->batch == 0) return MLA_OK;
+  if (!q_nope || !q_rope || !positions || !k_nope || !v || !rope_cache || !o)
+    return MLA_ERR_INVALID_ARG;
+  st = check_cache_args(dims, kv_row_stride, seq_lens, block_table, max_blocks_per_seq, block_size,
+                        max_seq_len);
+  if (st) return st;
+  if (causal != 0 && causal != 1) return MLA_ERR_INVALID_ARG;
+  if (!(softmax_scale > 0.f) || !isfinite(softmax_scale)) return MLA_ERR_INVALID_ARG;
+  if (!(rope_base > 0.f) || !isfinite(rope_base)) return MLA_ERR_INVALID_ARG;
+  if (!aligned16(q_nope) || !aligned16(q_rope) || !aligned16(k_nope) || !aligned16(v) ||
+      !aligned16(rope_cache) || !aligned16(o))
+    return MLA_ERR_INVALID_ARG;
+  if (!prefill_supports(*dims, kv_row_stride, max_seq_len)) return MLA_ERR_UNSUPPORTED;
+  PrefillArgs a{};
+  a.rope = rope_cache;
+  a.row_stride = kv_row_stride;
+  a.seq_lens = seq_lens;
+  a.block_table = block_table;
+  a.mbps = max_blocks_per_seq;
+  a.max_seq_len = max_seq_len;
+  a.batch = dims->batch;
+  a.q_len = dims->q_len;
+  a.heads = dims->heads;
+  a.causal = causal;
+  a.softmax_scale = softmax_scale;
+  a.k_nope = const_cast<void*>(k_nope);
+  a.v = const_cast<void*>(v);
+  a.q_nope = q_nope;
+  a.q_rope = q_rope;
+  a.positions = positions;
+  a.rope_base = rope_base;
+  a.o = o;
+  a.lse = lse;
+  (void)hipGetLastError();
+  return launched(launch_prefill_attn(*dims, a, (hipStream_t)stream));
 }
 
 }  // extern "C"

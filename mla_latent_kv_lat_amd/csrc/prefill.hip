@@ -1,0 +1,423 @@
+// MLA prefill in MHA form for gfx950 (bf16; d_nope = d_v = 128, d_rope = 64,
+// d_latent = 512).
+//
+// Pages cited (title, section):
+//   [ARCH] "Model Architecture Driving Inference Systems: From MHA/GQA to
+//          DeepSeek MLA Matrix Absorption and Memory Minimalism" (FAQ on
+//          prefill: absorbing there multiplies the attention flops by the
+//          ratio of latent to head width, ~4x)
+//   [DUAL] "DeepSeek's attention evolution - [MLA]" 2.5 (prefill runs the
+//          "MHA form": the latent is expanded into per-head keys and values;
+//          decode runs the absorbed "MQA form")
+//
+// Two kernels, one per ABI call:
+//
+// prefill_expand_kernel: k_nope[b,t,h,:] = W_UK,h c_t and v[b,t,h,:] = W_UV,h c_t
+//   for every cached token, one GEMM of the tokens' latents (K = 512) against
+//   the 2H x 128 rows of W_UK and W_UV.  Workgroup = 128 tokens of one
+//   sequence x one head's 128 k or v channels, 4 waves of 64 x 64 on
+//   v_mfma_f32_32x32x16_bf16; both operands stream through LDS in 64-wide k
+//   chunks (direct global->LDS loads, double buffered).
+//
+// prefill_attn_kernel: causal attention of the Lq prompt tokens of each
+//   sequence over its keys [k_nope ; k_rope] (192 wide, the decoupled RoPE
+//   key shared by the heads) and values (128 wide).  Workgroup = 256 query
+//   rows of one (sequence, head), 16 waves of 16 rows; the keys and values of
+//   32 tokens at a time are filled into LDS once for all 256 rows.  Each wave
+//   computes S^T = K Q^T, the online softmax and O^T += V^T P^T on
+//   v_mfma_f32_16x16x32_bf16 with P fed from the score registers, exactly as
+//   the decode kernel does with the latent (same LDS layout and operand
+//   addressing).
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "common.hpp"
+#include "decode_common.hpp"
+#include "kernels.hpp"
+#include "mfma_common.hpp"
+
+namespace mla {
+namespace {
+
+using namespace mfma;
+using namespace dec;
+
+// ------------------------------------------------------------------ expand
+
+constexpr int kExTok = 128;                  // tokens per workgroup
+constexpr int kExKc = 64;                    // k per LDS chunk
+constexpr int kExOpBytes = 128 * kExKc * 2;  // 16 KB: one operand's chunk
+constexpr int kExBytes = 2 * 2 * kExOpBytes; // two buffers of A and B
+
+// 1 KB LDS block = 8 rows x 8 16-byte chunks; row rho, chunk kappa at entry
+// 8 rho + (kappa ^ rho), so a 32x32x16 operand read (32 rows, one chunk) and
+// the wave-wide fill (lane e -> row e/8, chunk (e%8) ^ row) are free of bank
+// conflicts.
+__device__ __forceinline__ uint32_t ex_entry(int row, int kap) {
+  return (uint32_t)((row >> 3) * 1024 + 16 * (8 * (row & 7) + (kap ^ (row & 7))));
+}
+
+__global__ __launch_bounds__(256) void prefill_expand_kernel(PrefillArgs a) {
+  __shared__ __attribute__((aligned(1024))) char smem[kExBytes];
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int H = a.heads;
+  const int cb = blockIdx.x;                 // channel block: W_UK,h (cb < H) or W_UV,h
+  const int b = (int)(blockIdx.y / a.ntile);
+  const int t0 = (int)(blockIdx.y % a.ntile) * kExTok;
+  const int len = a.seq_lens[b];
+  if (t0 >= len) return;  // uniform across the workgroup
+  const bool is_v = cb >= H;
+  const int h = is_v ? cb - H : cb;
+  const uint16_t* wsrc = (is_v ? a.w_uv : a.w_uk) + (int64_t)h * 128 * 512;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_char*)smem;
+
+  // first cache row of the tile's two 64-token pages (the second only when
+  // the sequence reaches it)
+  auto page_row = [&](int page) -> int64_t {
+    return a.block_table ? (int64_t)a.block_table[(int64_t)b * a.mbps + page] * kTile
+                         : (int64_t)b * a.max_seq_len + (int64_t)page * kTile;
+  };
+  const int pg0 = t0 >> 6;
+  const int64_t prow0 = page_row(pg0);
+  const int64_t prow1 = t0 + kTile < len ? page_row(pg0 + 1) : prow0;
+
+  // fill lane: row e/8 of a block, chunk (e%8) ^ row
+  const int frow = lane >> 3, fkap = (lane & 7) ^ frow;
+  // block j of a chunk: j < 16 the tokens' latents (rows 8j..), else the
+  // weight rows 8(j-16)..; wave w issues j = w, w+4, .., w+28
+  auto issue = [&](int kc, int buf) {
+    const uint32_t dst = lds0 + (uint32_t)(buf * 2 * kExOpBytes);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int j = w + 4 * i;
+      if (j < 16) {
+        // the block's rows, clamped to the sequence's last token (a whole
+        // block past the end re-reads it); all in one page
+        const int tb = min(t0 + 8 * j, len - 1);
+        const int ps = tb & ~(kTile - 1);
+        const int64_t r0 = (tb >> 6) == pg0 ? prow0 : prow1;
+        const int tl = min(t0 + 8 * j + frow, len - 1) - ps;
+        const char* base = (const char*)a.latent + r0 * a.row_stride * 2;
+        const uint32_t voff = (uint32_t)(tl * a.row_stride * 2) + (uint32_t)((kc * kExKc + fkap * 8) * 2);
+        lds_dma16(base, voff, dst + (uint32_t)(j * 1024));
+      } else {
+        const int jr = j - 16;
+        const uint32_t voff = (uint32_t)(((8 * jr + frow) * 512 + kc * kExKc + fkap * 8) * 2);
+        lds_dma16(wsrc, voff, dst + (uint32_t)(kExOpBytes + jr * 1024));
+      }
+    }
+  };
+
+  const int wr = w >> 1, wc = w & 1;  // wave tile: tokens 64 wr.., channels 64 wc..
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni) acc[mi][ni] = f32x16{};
+
+  issue(0, 0);
+  constexpr int kChunks = 512 / kExKc;
+  for (int kc = 0; kc < kChunks; ++kc) {
+    if (kc + 1 < kChunks) issue(kc + 1, (kc + 1) & 1);
+    if (kc + 1 < kChunks)
+      wait_vm(8);  // this wave's loads of chunk kc landed (those of kc+1 in flight)
+    else
+      wait_vm(0);
+    block_sync();
+    const char* A = smem + (kc & 1) * 2 * kExOpBytes;
+    const char* Bm = A + kExOpBytes;
+    const int l32 = lane & 31, hk = lane >> 5;
+#pragma unroll
+    for (int ks = 0; ks < kExKc / 16; ++ks) {
+      const int kap = 2 * ks + hk;
+      bf16x8 av[2], bv[2];
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi)
+        av[mi] = *(const bf16x8*)(A + ex_entry(64 * wr + 32 * mi + l32, kap));
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni)
+        bv[ni] = *(const bf16x8*)(Bm + ex_entry(64 * wc + 32 * ni + l32, kap));
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni) acc[mi][ni] = mfma32(av[mi], bv[ni], acc[mi][ni]);
+    }
+    block_sync();  // the buffer is refilled by the loads of chunk kc+2
+  }
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni) mfma_settle(acc[mi][ni]);
+
+  // C (32 x 32): lane l holds channel l%32, tokens 8(r/4) + 4(l/32) + r%4
+  uint16_t* dst = (uint16_t*)(is_v ? a.v : a.k_nope);
+  const int ch = lane & 31, hr = lane >> 5;
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int t = t0 + 64 * wr + 32 * mi + 8 * (r >> 2) + 4 * hr + (r & 3);
+      if (t < len) {
+        uint16_t* row = dst + (((int64_t)b * a.max_seq_len + t) * H + h) * 128 + 64 * wc + ch;
+        row[0] = f32_to_bf16(acc[mi][0][r]);
+        row[32] = f32_to_bf16(acc[mi][1][r]);
+      }
+    }
+}
+
+// --------------------------------------------------------------- attention
+
+constexpr int kAtWaves = 16;
+constexpr int kAtRows = 16 * kAtWaves;          // 256 query rows per workgroup
+constexpr int kAtSub = 32;                      // tokens per LDS sub-tile
+constexpr int kAtKBytes = kAtSub * 192 * 2;     // 12 KB: keys, column groups 0-2
+constexpr int kAtSubBytes = kAtKBytes + kAtSub * 128 * 2;  // + 8 KB values
+constexpr int kAtRing = 4;
+constexpr int kAtMaxPages = 4096;               // 262144 tokens
+constexpr int kAtBytes = kAtRing * kAtSubBytes + kAtMaxPages * 4;
+static_assert(kAtBytes <= 163840, "LDS budget");
+
+__global__ __launch_bounds__(1024) void prefill_attn_kernel(PrefillArgs a) {
+  __shared__ __attribute__((aligned(1024))) char smem[kAtBytes];
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int H = a.heads, Lq = a.q_len;
+  const int nqb = (Lq + kAtRows - 1) / kAtRows;
+  const int qb = nqb - 1 - (int)blockIdx.x;  // the longest causal ranges first
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int len = a.seq_lens[b];
+  const int i0 = qb * kAtRows;
+  const int64_t Tmax = a.max_seq_len;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_char*)smem;
+  int* prow = (int*)(smem + kAtRing * kAtSubBytes);  // block id (paged) of each page
+
+  // visible tokens of query i: t < len - Lq + i + 1 (causal) or t < len
+  auto n_vis = [&](int i) { return a.causal ? len - Lq + i + 1 : len; };
+  const int i_last = min(Lq, i0 + kAtRows) - 1;
+  const int n_end = min(len, max(0, n_vis(i_last)));  // tokens the workgroup reads
+  const int nsub = (n_end + kAtSub - 1) / kAtSub;
+
+  // rows of this wave; lane l holds row i0 + 16w + l%16
+  const int wrow0 = i0 + 16 * w;
+  const bool active = wrow0 < Lq;  // uniform per wave
+  const int wave_vis = active ? min(len, max(0, n_vis(min(wrow0 + 15, Lq - 1)))) : 0;
+
+  // ---- the wave's query rows: q_nope in k-slices 0-3, RoPE(q_rope) in 4-5
+  bf16x8 q[6];
+  {
+    const int li = lane & 15, g = lane >> 4;
+    const int i = min(wrow0 + li, Lq - 1);
+    const int64_t qrow = ((int64_t)b * Lq + i) * H + h;
+    const bf16x8* qn = (const bf16x8*)((const uint16_t*)a.q_nope + qrow * 128);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) q[kk] = qn[4 * kk + g];
+    const bf16x8* qr = (const bf16x8*)((const uint16_t*)a.q_rope + qrow * 64);
+    const double pos = (double)a.positions[(int64_t)b * Lq + i];
+    const double l2b = log2((double)a.rope_base);
+#pragma unroll
+    for (int kk = 4; kk < 6; ++kk) {
+      const bf16x8 x = qr[4 * (kk - 4) + g];
+      bf16x8 y;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        // pair p = 16 (kk-4) + 4 g + m turns by pos * base^(-2p/64); the
+        // angle is reduced modulo 2 pi in double, sin/cos in single
+        const int p = 16 * (kk - 4) + 4 * g + m;
+        double ang = pos * exp2(-2.0 * p / 64.0 * l2b);
+        ang -= 6.283185307179586 * rint(ang * 0.15915494309189535);
+        float sn, cs;
+        __sincosf((float)ang, &sn, &cs);
+        const float x0 = (float)x[2 * m], x1 = (float)x[2 * m + 1];
+        y[2 * m] = (__bf16)(x0 * cs - x1 * sn);
+        y[2 * m + 1] = (__bf16)(x0 * sn + x1 * cs);
+      }
+      q[kk] = y;
+    }
+#pragma unroll
+    for (int kk = 0; kk < 6; ++kk) asm volatile("" ::"v"(q[kk]));  // loaded before the fills go out
+  }
+  // page table of the tokens this workgroup reads
+  if (a.block_table) {
+    const int npg = (n_end + kTile - 1) / kTile;
+    for (int p = (int)threadIdx.x; p < npg; p += 1024) prow[p] = a.block_table[(int64_t)b * a.mbps + p];
+  }
+  wait_vm0();
+  block_sync();
+
+  // ---- fills: 20 blocks of 1 KB per sub-tile (keys: column groups 0-1
+  // k_nope, 2 the RoPE key; values: 0-1), block k by wave k % 16; all of a
+  // wave's blocks are row group w & 3
+  const int n_share = w < 4 ? 2 : 1;
+  const int rg = w & 3;
+  const int kap = (lane >> 3) ^ (rg & 1);
+  const int rho = (lane & 7) ^ (4 * ((kap ^ (kap >> 1)) & 1));
+  int pz = 0;  // next sub-tile to fill
+  auto issue = [&]() {
+    const int t0 = pz * kAtSub;
+    const uint32_t slot = lds0 + (uint32_t)((pz & (kAtRing - 1)) * kAtSubBytes);
+    const int tl = min(t0 + 8 * rg + rho, len - 1) - t0;  // clamped rows are masked
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int k = w + 16 * i;
+      if (k >= 20) break;  // uniform
+      if (k < 8 || k >= 12) {  // k_nope or v: [B, Tmax, H, 128]
+        const int cg = (k < 8 ? k : k - 12) >> 2;
+        const char* base = (const char*)(k < 8 ? a.k_nope : a.v) + (((int64_t)b * Tmax + t0) * H + h) * 256;
+        const uint32_t voff = (uint32_t)(tl * H * 256) + (uint32_t)((cg * 64 + kap * 8) * 2);
+        lds_dma16_stream(base, voff, slot + (uint32_t)((k < 8 ? 0 : kAtKBytes) + (cg * 4 + rg) * 1024));
+      } else {  // RoPE key of the cache rows (one page holds the sub-tile)
+        const int ps = t0 & ~(kTile - 1);
+        const int64_t r0 = a.block_table ? (int64_t)prow[t0 >> 6] * kTile : (int64_t)b * Tmax + ps;
+        const char* base = (const char*)a.rope + r0 * a.row_stride * 2;
+        const uint32_t voff = (uint32_t)((t0 - ps + tl) * a.row_stride * 2) + (uint32_t)(kap * 16);
+        lds_dma16_stream(base, voff, slot + (uint32_t)((2 * 4 + rg) * 1024));
+      }
+    }
+    ++pz;
+  };
+
+  for (int z = 0; z < kAtRing - 1 && z < nsub; ++z) issue();
+  if (nsub > 0) wait_vm(n_share * (pz - 1));
+  block_sync();
+
+  f32x4 o[8];  // O^T: block nb holds value columns 16 nb + 4(l/16)..+3 of row l%16
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb) o[nb] = f32x4{};
+  float m_run = -INFINITY, l_run = 0.f;
+  const float sl2 = a.softmax_scale * kLog2e;
+
+  for (int s = 0; s < nsub; ++s) {
+    if (s + kAtRing - 1 < nsub) issue();  // into the slot every wave finished with
+    const char* tile = smem + (s & (kAtRing - 1)) * kAtSubBytes;
+    const int t0 = s * kAtSub;
+    if (active && t0 < wave_vis) {  // uniform per wave
+      f32x4 sc[2] = {f32x4{}, f32x4{}};  // token block jt: tokens 16 jt + 4(l/16)..+3
+      {
+        constexpr int kPf = 2;
+        const uint32_t o_qk = off_qk(fresh_lane());
+        bf16x8 ka[kPf + 1][2];
+        auto kload = [&](int kk) {
+          const int e = kk % (kPf + 1);
+#pragma unroll
+          for (int jt = 0; jt < 2; ++jt)
+            ka[e][jt] = *(const bf16x8*)(tile + (uint32_t)((kk >> 1) * 4096 + 2048 * jt + 512 * (kk & 1)) + o_qk);
+        };
+#pragma unroll
+        for (int kk = 0; kk < kPf; ++kk) kload(kk);
+#pragma unroll
+        for (int kk = 0; kk < 6; ++kk) {
+          if (kk + kPf < 6) kload(kk + kPf);
+          const int e = kk % (kPf + 1);
+          sc[0] = mfma16(ka[e][0], q[kk], sc[0]);
+          sc[1] = mfma16(ka[e][1], q[kk], sc[1]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        mfma_settle(sc[0]);
+        mfma_settle(sc[1]);
+      }
+      const int ln = fresh_lane();
+      const int nv = n_vis(wrow0 + (ln & 15));  // this lane's row
+      if (t0 + kAtSub > min(nv, len) || t0 + kAtSub > wave_vis) {  // mask past the visible end
+#pragma unroll
+        for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int t = t0 + 16 * jt + 4 * (ln >> 4) + r;
+            if (t >= nv || t >= len) sc[jt][r] = -INFINITY;
+          }
+      }
+      // lazy rescale: the reference max moves only when a score passes it
+      // by more than 2^8 (log2 units)
+      const float lm = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
+                             fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3]))) * sl2;
+      if (__ballot(lm > m_run + 8.f) != 0) {
+        float mt = fmaxf(lm, __shfl_xor(lm, 16, 64));
+        mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+        const float m_new = fmaxf(m_run, mt);
+        const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) o[nb] *= alpha;
+      }
+      const float m_use = m_run == -INFINITY ? 0.f : m_run;
+      bf16x8 p;  // P^T operand: tokens {4(l/16)..+3, 16+4(l/16)..+3} of row l%16
+#pragma unroll
+      for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float e = __builtin_amdgcn_exp2f(fmaf(sc[jt][r], sl2, -m_use));
+          l_run += e;
+          p[4 * jt + r] = (__bf16)e;
+        }
+      // O^T += V^T P^T, V^T read transposed from the values' blocks
+      const char* vt = tile + kAtKBytes;
+      const int lv = fresh_lane();
+      const uint32_t vb00 = vt_base(lv, 0, 0), vb01 = vt_base(lv, 0, 1);
+      const uint32_t vb10 = vt_base(lv, 1, 0), vb11 = vt_base(lv, 1, 1);
+      auto vload = [&](int nb) {
+        const uint32_t cb = (uint32_t)((nb >> 2) * 4096 + (nb & 3) * 256);
+        return cat(lds_tr4(vt, cb + ((nb & 1) ? vb01 : vb00)), lds_tr4(vt, cb + ((nb & 1) ? vb11 : vb10)));
+      };
+      bf16x8 va = vload(0), vn = vload(1);
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) {
+        const bf16x8 vnn = nb + 2 < 8 ? vload(nb + 2) : vn;
+        o[nb] = mfma16(va, p, o[nb]);
+        __builtin_amdgcn_sched_barrier(0);
+        va = vn;
+        vn = vnn;
+      }
+    }
+    // this wave's fills of sub-tile s+1 landed (later ones may stay in flight)
+    if (s + 1 < nsub) wait_vm(n_share * (pz - 1 - (s + 1)));
+    block_sync();  // sub-tile s+1 complete for everyone; the slot of s free
+  }
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb) mfma_settle(o[nb]);
+
+  // ---- outputs: o = O / l (0 where no token was visible), lse
+  float l_tot = l_run + __shfl_xor(l_run, 16, 64);
+  l_tot += __shfl_xor(l_tot, 32, 64);
+  const int lw = fresh_lane();
+  const int i = wrow0 + (lw & 15);
+  if (active && i < Lq) {
+    const int64_t row = ((int64_t)b * Lq + i) * H + h;
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    if (a.lse && (lw >> 4) == 0) a.lse[row] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+    uint16_t* orow = (uint16_t*)a.o + row * 128 + 4 * (lw >> 4);
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) {
+      const uint2 v2 = make_uint2((uint32_t)f32_to_bf16(o[nb][0] * inv) | ((uint32_t)f32_to_bf16(o[nb][1] * inv) << 16),
+                                  (uint32_t)f32_to_bf16(o[nb][2] * inv) | ((uint32_t)f32_to_bf16(o[nb][3] * inv) << 16));
+      *(uint2*)(orow + 16 * nb) = v2;
+    }
+  }
+}
+
+}  // namespace
+
+bool prefill_supports(const mla_dims_t& d, int64_t row_stride, int max_seq_len) {
+  return d.q_dtype == MLA_BF16 && d.kv_dtype == MLA_BF16 && d.d_nope == 128 && d.d_v == 128 &&
+         d.d_rope == 64 && d.d_latent == 512 && row_stride % 8 == 0 && row_stride <= (1 << 16) &&
+         (int64_t)d.heads * 256 * 32 < ((int64_t)1 << 31) && max_seq_len <= kAtMaxPages * kTile &&
+         (int64_t)d.batch * ((max_seq_len + kExTok - 1) / kExTok) <= 65535 && d.heads <= 32767;
+}
+
+hipError_t launch_prefill_expand(const mla_dims_t& d, const PrefillArgs& a, hipStream_t s) {
+  PrefillArgs x = a;
+  x.ntile = (a.max_seq_len + kExTok - 1) / kExTok;
+  dim3 grid((unsigned)(2 * d.heads), (unsigned)(d.batch * x.ntile));
+  hipLaunchKernelGGL(prefill_expand_kernel, grid, dim3(256), 0, s, x);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_attn(const mla_dims_t& d, const PrefillArgs& a, hipStream_t s) {
+  dim3 grid((unsigned)((d.q_len + kAtRows - 1) / kAtRows), (unsigned)d.heads, (unsigned)d.batch);
+  hipLaunchKernelGGL(prefill_attn_kernel, grid, dim3(1024), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace mla

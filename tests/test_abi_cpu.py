@@ -209,3 +209,49 @@ def test_kv_append_noalloc_validation():
     assert call(mla.append_dims(4, 7168, kv_dtype=mla.FP8_E4M3)) == 1
     assert "MLA_ERR_TOO_LARGE" in lib.mla_status_string(5).decode()
 
+
+def test_prefill_validation():
+    """The MHA-form prefill calls: host checks before anything is enqueued,
+    and shapes or types they are not built for rejected as unsupported."""
+    lib = binding._lib
+    ok = dict(q_nope=16, q_rope=16, positions=16, rope_base=10000.0, k_nope=16, v=16,
+              rope_cache=16, latent_cache=16, kv_row_stride=576, seq_lens=16, block_table=None,
+              max_blocks_per_seq=0, block_size=64, max_seq_len=256, causal=1,
+              softmax_scale=0.07, o=16, lse=None, w_uk=16, w_uv=16)
+
+    def attn(dd, **kw):
+        a = dict(ok, **kw)
+        return lib.mla_prefill_attn(ctypes.byref(dd), a["q_nope"], a["q_rope"], a["positions"],
+                                    a["rope_base"], a["k_nope"], a["v"], a["rope_cache"],
+                                    a["kv_row_stride"], a["seq_lens"], a["block_table"],
+                                    a["max_blocks_per_seq"], a["block_size"], a["max_seq_len"],
+                                    a["causal"], a["softmax_scale"], a["o"], a["lse"], None)
+
+    def expand(dd, **kw):
+        a = dict(ok, **kw)
+        return lib.mla_prefill_expand(ctypes.byref(dd), a["latent_cache"], a["kv_row_stride"],
+                                      a["seq_lens"], a["block_table"], a["max_blocks_per_seq"],
+                                      a["block_size"], a["max_seq_len"], a["w_uk"], a["w_uv"],
+                                      a["k_nope"], a["v"], None)
+
+    d = _d(q_len=256)
+    for call in (attn, expand):
+        assert call(_d(batch=0)) == 0                            # nothing to do
+        assert call(d, seq_lens=None) == 1
+        assert call(d, kv_row_stride=100) == 1
+        assert call(d, max_seq_len=0) == 1
+        assert call(d, block_table=16, block_size=32, max_blocks_per_seq=4) == 1
+        assert call(d, block_table=16, block_size=64, max_blocks_per_seq=3) == 1  # 3 x 64 < 256
+        assert call(d, k_nope=8) == 1                            # misaligned
+        assert call(_d(q_len=256, kv_dtype=mla.FP8_E4M3)) == 2
+        assert call(_d(q_len=256, d_nope=64)) == 2
+        assert call(_d(q_len=256, d_latent=256)) == 2
+        assert call(d, max_seq_len=262145) == 2
+        assert call(d, kv_row_stride=580) == 2                   # rows not 16-byte aligned
+    assert attn(d, q_rope=None) == 1
+    assert attn(d, o=None) == 1
+    assert attn(d, causal=2) == 1
+    assert attn(d, softmax_scale=0.0) == 1
+    assert attn(d, rope_base=float("inf")) == 1
+    assert expand(d, w_uv=None) == 1
+    assert attn(_d(q_len=256, q_dtype=mla.F32, kv_dtype=mla.F32)) == 2
