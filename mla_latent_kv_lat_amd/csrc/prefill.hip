@@ -23,7 +23,7 @@
 //   sequence over its keys [k_nope ; k_rope] (192 wide, the decoupled RoPE
 //   key shared by the heads) and values (128 wide).  Workgroup = 256 query
 //   rows of one (sequence, head), 16 waves of 16 rows; the keys and values of
-//   32 tokens at a time are filled into LDS once for all 256 rows.  Each wave
+//   64 tokens (one page) at a time are filled into LDS once for all 256 rows.  Each wave
 //   computes S^T = K Q^T, the online softmax and O^T += V^T P^T on
 //   v_mfma_f32_16x16x32_bf16 with P fed from the score registers, exactly as
 //   the decode kernel does with the latent (same LDS layout and operand
@@ -171,10 +171,11 @@ __global__ __launch_bounds__(256) void prefill_expand_kernel(PrefillArgs a) {
 
 constexpr int kAtWaves = 16;
 constexpr int kAtRows = 16 * kAtWaves;          // 256 query rows per workgroup
-constexpr int kAtSub = 32;                      // tokens per LDS sub-tile
-constexpr int kAtKBytes = kAtSub * 192 * 2;     // 12 KB: keys, column groups 0-2
-constexpr int kAtSubBytes = kAtKBytes + kAtSub * 128 * 2;  // + 8 KB values
-constexpr int kAtRing = 4;
+constexpr int kAtSub = 64;                      // tokens per LDS sub-tile (one page)
+constexpr int kAtCg = kAtSub * 128;             // 8 KB: one 64-column group of the sub-tile
+constexpr int kAtKBytes = 3 * kAtCg;            // 24 KB: keys, column groups 0-2
+constexpr int kAtSubBytes = kAtKBytes + 2 * kAtCg;  // + 16 KB values
+constexpr int kAtRing = 3;
 constexpr int kAtMaxPages = 4096;               // 262144 tokens
 constexpr int kAtBytes = kAtRing * kAtSubBytes + kAtMaxPages * 4;
 static_assert(kAtBytes <= 163840, "LDS budget");
@@ -246,33 +247,32 @@ __global__ __launch_bounds__(1024) void prefill_attn_kernel(PrefillArgs a) {
   wait_vm0();
   block_sync();
 
-  // ---- fills: 20 blocks of 1 KB per sub-tile (keys: column groups 0-1
-  // k_nope, 2 the RoPE key; values: 0-1), block k by wave k % 16; all of a
-  // wave's blocks are row group w & 3
-  const int n_share = w < 4 ? 2 : 1;
-  const int rg = w & 3;
+  // ---- fills: 40 blocks of 1 KB per sub-tile (keys: column groups 0-1
+  // k_nope, 2 the RoPE key; values: 0-1; 8 row groups each), block k by
+  // wave k % 16; all of a wave's blocks are row group w & 7
+  const int n_share = w < 8 ? 3 : 2;
+  const int rg = w & 7;
   const int kap = (lane >> 3) ^ (rg & 1);
   const int rho = (lane & 7) ^ (4 * ((kap ^ (kap >> 1)) & 1));
   int pz = 0;  // next sub-tile to fill
   auto issue = [&]() {
     const int t0 = pz * kAtSub;
-    const uint32_t slot = lds0 + (uint32_t)((pz & (kAtRing - 1)) * kAtSubBytes);
+    const uint32_t slot = lds0 + (uint32_t)((pz % kAtRing) * kAtSubBytes);
     const int tl = min(t0 + 8 * rg + rho, len - 1) - t0;  // clamped rows are masked
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < 3; ++i) {
       const int k = w + 16 * i;
-      if (k >= 20) break;  // uniform
-      if (k < 8 || k >= 12) {  // k_nope or v: [B, Tmax, H, 128]
-        const int cg = (k < 8 ? k : k - 12) >> 2;
-        const char* base = (const char*)(k < 8 ? a.k_nope : a.v) + (((int64_t)b * Tmax + t0) * H + h) * 256;
+      if (k >= 40) break;  // uniform
+      if (k < 16 || k >= 24) {  // k_nope or v: [B, Tmax, H, 128]
+        const int cg = (k < 16 ? k : k - 24) >> 3;
+        const char* base = (const char*)(k < 16 ? a.k_nope : a.v) + (((int64_t)b * Tmax + t0) * H + h) * 256;
         const uint32_t voff = (uint32_t)(tl * H * 256) + (uint32_t)((cg * 64 + kap * 8) * 2);
-        lds_dma16_stream(base, voff, slot + (uint32_t)((k < 8 ? 0 : kAtKBytes) + (cg * 4 + rg) * 1024));
-      } else {  // RoPE key of the cache rows (one page holds the sub-tile)
-        const int ps = t0 & ~(kTile - 1);
-        const int64_t r0 = a.block_table ? (int64_t)prow[t0 >> 6] * kTile : (int64_t)b * Tmax + ps;
+        lds_dma16_stream(base, voff, slot + (uint32_t)((k < 16 ? 0 : kAtKBytes) + cg * kAtCg + rg * 1024));
+      } else {  // RoPE key of the cache rows (the sub-tile is one page)
+        const int64_t r0 = a.block_table ? (int64_t)prow[t0 >> 6] * kTile : (int64_t)b * Tmax + t0;
         const char* base = (const char*)a.rope + r0 * a.row_stride * 2;
-        const uint32_t voff = (uint32_t)((t0 - ps + tl) * a.row_stride * 2) + (uint32_t)(kap * 16);
-        lds_dma16_stream(base, voff, slot + (uint32_t)((2 * 4 + rg) * 1024));
+        const uint32_t voff = (uint32_t)(tl * a.row_stride * 2) + (uint32_t)(kap * 16);
+        lds_dma16_stream(base, voff, slot + (uint32_t)(2 * kAtCg + rg * 1024));
       }
     }
     ++pz;
@@ -290,19 +290,21 @@ __global__ __launch_bounds__(1024) void prefill_attn_kernel(PrefillArgs a) {
 
   for (int s = 0; s < nsub; ++s) {
     if (s + kAtRing - 1 < nsub) issue();  // into the slot every wave finished with
-    const char* tile = smem + (s & (kAtRing - 1)) * kAtSubBytes;
+    const char* tile = smem + (s % kAtRing) * kAtSubBytes;
     const int t0 = s * kAtSub;
     if (active && t0 < wave_vis) {  // uniform per wave
-      f32x4 sc[2] = {f32x4{}, f32x4{}};  // token block jt: tokens 16 jt + 4(l/16)..+3
+      f32x4 sc[4];  // token block jt: tokens 16 jt + 4(l/16)..+3
+#pragma unroll
+      for (int jt = 0; jt < 4; ++jt) sc[jt] = f32x4{};
       {
         constexpr int kPf = 2;
         const uint32_t o_qk = off_qk(fresh_lane());
-        bf16x8 ka[kPf + 1][2];
+        bf16x8 ka[kPf + 1][4];
         auto kload = [&](int kk) {
           const int e = kk % (kPf + 1);
 #pragma unroll
-          for (int jt = 0; jt < 2; ++jt)
-            ka[e][jt] = *(const bf16x8*)(tile + (uint32_t)((kk >> 1) * 4096 + 2048 * jt + 512 * (kk & 1)) + o_qk);
+          for (int jt = 0; jt < 4; ++jt)
+            ka[e][jt] = *(const bf16x8*)(tile + (uint32_t)((kk >> 1) * kAtCg + 2048 * jt + 512 * (kk & 1)) + o_qk);
         };
 #pragma unroll
         for (int kk = 0; kk < kPf; ++kk) kload(kk);
@@ -310,28 +312,30 @@ __global__ __launch_bounds__(1024) void prefill_attn_kernel(PrefillArgs a) {
         for (int kk = 0; kk < 6; ++kk) {
           if (kk + kPf < 6) kload(kk + kPf);
           const int e = kk % (kPf + 1);
-          sc[0] = mfma16(ka[e][0], q[kk], sc[0]);
-          sc[1] = mfma16(ka[e][1], q[kk], sc[1]);
+#pragma unroll
+          for (int jt = 0; jt < 4; ++jt) sc[jt] = mfma16(ka[e][jt], q[kk], sc[jt]);
           __builtin_amdgcn_sched_barrier(0);
         }
-        mfma_settle(sc[0]);
-        mfma_settle(sc[1]);
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt) mfma_settle(sc[jt]);
       }
       const int ln = fresh_lane();
-      const int nv = n_vis(wrow0 + (ln & 15));  // this lane's row
-      if (t0 + kAtSub > min(nv, len) || t0 + kAtSub > wave_vis) {  // mask past the visible end
+      const int nv = min(len, n_vis(wrow0 + (ln & 15)));  // this lane's row
+      if (t0 + kAtSub > nv) {  // mask past the visible end
 #pragma unroll
-        for (int jt = 0; jt < 2; ++jt)
+        for (int jt = 0; jt < 4; ++jt)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int t = t0 + 16 * jt + 4 * (ln >> 4) + r;
-            if (t >= nv || t >= len) sc[jt][r] = -INFINITY;
-          }
+          for (int r = 0; r < 4; ++r)
+            if (t0 + 16 * jt + 4 * (ln >> 4) + r >= nv) sc[jt][r] = -INFINITY;
       }
       // lazy rescale: the reference max moves only when a score passes it
       // by more than 2^8 (log2 units)
-      const float lm = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
-                             fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3]))) * sl2;
+      float lm = sc[0][0];
+#pragma unroll
+      for (int jt = 0; jt < 4; ++jt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) lm = fmaxf(lm, sc[jt][r]);
+      lm *= sl2;
       if (__ballot(lm > m_run + 8.f) != 0) {
         float mt = fmaxf(lm, __shfl_xor(lm, 16, 64));
         mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
@@ -343,29 +347,33 @@ __global__ __launch_bounds__(1024) void prefill_attn_kernel(PrefillArgs a) {
         for (int nb = 0; nb < 8; ++nb) o[nb] *= alpha;
       }
       const float m_use = m_run == -INFINITY ? 0.f : m_run;
-      bf16x8 p;  // P^T operand: tokens {4(l/16)..+3, 16+4(l/16)..+3} of row l%16
+      // P^T operands of the two 32-token halves ks: tokens
+      // {32 ks + 4(l/16)..+3, 32 ks + 16 + 4(l/16)..+3} of row l%16
+      bf16x8 p[2];
 #pragma unroll
-      for (int jt = 0; jt < 2; ++jt)
+      for (int jt = 0; jt < 4; ++jt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const float e = __builtin_amdgcn_exp2f(fmaf(sc[jt][r], sl2, -m_use));
           l_run += e;
-          p[4 * jt + r] = (__bf16)e;
+          p[jt >> 1][4 * (jt & 1) + r] = (__bf16)e;
         }
-      // O^T += V^T P^T, V^T read transposed from the values' blocks
+      // O^T += V^T P^T, V^T read transposed from the values' blocks (the
+      // second half's row groups sit 4 KB after the first's)
       const char* vt = tile + kAtKBytes;
       const int lv = fresh_lane();
       const uint32_t vb00 = vt_base(lv, 0, 0), vb01 = vt_base(lv, 0, 1);
       const uint32_t vb10 = vt_base(lv, 1, 0), vb11 = vt_base(lv, 1, 1);
-      auto vload = [&](int nb) {
-        const uint32_t cb = (uint32_t)((nb >> 2) * 4096 + (nb & 3) * 256);
+      auto vload = [&](int n) {  // n = 2 nb + ks
+        const int nb = n >> 1, ks = n & 1;
+        const uint32_t cb = (uint32_t)((nb >> 2) * kAtCg + ks * 4096 + (nb & 3) * 256);
         return cat(lds_tr4(vt, cb + ((nb & 1) ? vb01 : vb00)), lds_tr4(vt, cb + ((nb & 1) ? vb11 : vb10)));
       };
       bf16x8 va = vload(0), vn = vload(1);
 #pragma unroll
-      for (int nb = 0; nb < 8; ++nb) {
-        const bf16x8 vnn = nb + 2 < 8 ? vload(nb + 2) : vn;
-        o[nb] = mfma16(va, p, o[nb]);
+      for (int n = 0; n < 16; ++n) {
+        const bf16x8 vnn = n + 2 < 16 ? vload(n + 2) : vn;
+        o[n >> 1] = mfma16(va, p[n & 1], o[n >> 1]);
         __builtin_amdgcn_sched_barrier(0);
         va = vn;
         vn = vnn;
