@@ -3,6 +3,9 @@
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 
+`--workload prefill_b4_s4k` measures the MHA-form prefill instead (a step
+is mla_prefill_expand + mla_prefill_attn; value in TFLOP/s).
+
 A step is the whole hot path on one batch of synthetic inputs already
 resident in GPU memory: mla_absorb_q (W_UK absorption + query RoPE),
 mla_decode_attn (split-K attention over the shared latent cache) and
@@ -163,6 +166,174 @@ def append_pass(mla, stream, n_tok: int, d_model: int, flush, reps: int) -> dict
             "kernels": "kv_down_kernel + kv_finish_kernel"}
 
 
+def prefill_accounting(inp):
+    """Flops of the MHA-form prefill: the expand GEMM over every cached token
+    (H x (d_nope + d_v) outputs of width d_latent) and the causal attention
+    (scores over d_nope + d_rope, values over d_v, visible pairs only)."""
+    c = inp.cfg
+    tokens = int(inp.seq_lens.astype(np.int64).sum())
+    expand = 2.0 * tokens * c.d_latent * c.heads * (c.d_nope + c.d_v)
+    pairs = 0
+    for b in range(c.batch):
+        n = int(inp.seq_lens[b])
+        vis = np.arange(c.q_len) + n - c.q_len + 1 if c.causal else np.full(c.q_len, n)
+        pairs += int(np.clip(vis, 0, n).sum())
+    attn = 2.0 * c.heads * pairs * (c.d_nope + c.d_rope + c.d_v)
+    return dict(tokens=tokens, expand_flops=expand, attn_flops=attn, pairs=pairs)
+
+
+def prefill_main(args, name, torch):
+    """One MHA-form prefill (mla_prefill_expand + mla_prefill_attn) of the
+    prompt workload; a step is both calls.  Prints one JSON line."""
+    import mla_latent_kv_lat_amd as mla
+    from mla_inputs import PREFILL_CONFIGS, MLAInputs
+    from mla_inputs.device import to_device
+
+    cfg = PREFILL_CONFIGS[name]
+    t0 = time.perf_counter()
+    inp = MLAInputs(cfg)
+    dev = to_device(inp)
+    torch.cuda.synchronize()
+    log(f"[bench] inputs for {name} ready in {time.perf_counter() - t0:.1f} s")
+    d = mla.dims(cfg.batch, cfg.q_len, cfg.heads, cfg.d_nope, cfg.d_rope, cfg.d_latent, cfg.d_v,
+                 mla.BF16, mla.BF16)
+    T = dev.max_seq_len
+    k_nope = torch.empty((cfg.batch, T, cfg.heads, cfg.d_nope), dtype=torch.bfloat16, device="cuda")
+    v = torch.empty((cfg.batch, T, cfg.heads, cfg.d_v), dtype=torch.bfloat16, device="cuda")
+    o = torch.empty((cfg.batch, cfg.q_len, cfg.heads, cfg.d_v), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((cfg.batch, cfg.q_len, cfg.heads), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def expand():
+        mla.mla_prefill_expand(d, dev.latent, dev.kv_row_stride, dev.seq_lens, dev.block_table,
+                               dev.max_blocks_per_seq, mla.TILE_TOKENS, T, dev.w_uk, dev.w_uv,
+                               k_nope, v, stream)
+
+    def attn():
+        mla.mla_prefill_attn(d, dev.q_nope, dev.q_rope, dev.positions, dev.rope_base, k_nope, v,
+                             dev.rope, dev.kv_row_stride, dev.seq_lens, dev.block_table,
+                             dev.max_blocks_per_seq, mla.TILE_TOKENS, T, dev.causal,
+                             dev.softmax_scale, o, lse, stream)
+
+    for _ in range(args.warmup):
+        expand()
+        attn()
+    torch.cuda.synchronize()
+    t_settle = time.perf_counter()
+    settle_steps = 0
+    while (time.perf_counter() - t_settle) * 1e3 < args.settle_ms:
+        expand()
+        attn()
+        settle_steps += 1
+        torch.cuda.synchronize()
+    settle_ms = (time.perf_counter() - t_settle) * 1e3
+    if not torch.isfinite(o.float()).all():
+        raise RuntimeError("non-finite prefill output")
+
+    # timed region: K steps, events around each call on the stream
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for k in range(args.steps):
+        ev[k][0].record(stream)
+        expand()
+        ev[k][1].record(stream)
+        attn()
+        ev[k][2].record(stream)
+    torch.cuda.synchronize()
+    ex_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
+    at_ms = np.array([e[1].elapsed_time(e[2]) for e in ev])
+    step_ms = np.array([e[0].elapsed_time(e[2]) for e in ev])
+    ms = float(np.median(step_ms))
+    acc = prefill_accounting(inp)
+    flops = acc["expand_flops"] + acc["attn_flops"]
+    at_med = float(np.median(at_ms))
+    ex_med = float(np.median(ex_ms))
+    tflops = flops / (ms * 1e-3) / 1e12
+    at_tf = acc["attn_flops"] / (at_med * 1e-3) / 1e12
+    ex_tf = acc["expand_flops"] / (ex_med * 1e-3) / 1e12
+    traffic = None
+    tpath = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                         "prefill_attn_b4_s4k_counters.json")
+    if os.path.exists(tpath):
+        try:
+            with open(tpath) as f:
+                tr = json.load(f)
+            from mla_latent_kv_lat_amd.build import PREFILL_SOURCES, source_digest
+            if tr.get("source_digest") == source_digest(PREFILL_SOURCES) and tr.get("workload") == name:
+                traffic = tr.get("hbm_bytes_per_launch")
+        except Exception as e:  # a stale or unreadable summary just leaves traffic unknown
+            log(f"[bench] traffic summary not used: {e}")
+    out = {
+        "metric": f"MLA prefill (MHA form) TFLOP/s at B={cfg.batch}, S={cfg.q_len}, {cfg.heads} heads",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "settle_ms": round(settle_ms, 1),
+        "settle_steps": settle_steps,
+        "pct_mfma_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": name, "batch": cfg.batch, "prompt_tokens": cfg.q_len,
+                   "seq_len": cfg.max_seq_len, "heads": cfg.heads, "d_nope": cfg.d_nope,
+                   "d_rope": cfg.d_rope, "d_latent": cfg.d_latent, "d_v": cfg.d_v,
+                   "causal": bool(cfg.causal), "paged_block": 64 if cfg.paged else None,
+                   "parallelism": "single GPU",
+                   "flops": {"expand": acc["expand_flops"], "attention": acc["attn_flops"]}},
+        "kernels_us": {"prefill_expand": round(ex_med * 1e3, 1), "prefill_attn": round(at_med * 1e3, 1),
+                       "expand_tflops": round(ex_tf, 1),
+                       "timing": "median of events around each call"},
+        "roofline": {"bound": "mfma", "achieved": round(at_tf, 1), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(at_tf / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                     "kernel": "prefill_attn_kernel", "launch_us": round(at_med * 1e3, 1),
+                     "timing": "median of events around each launch, on its stream"},
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a sample ...")
+        out["cpu_baseline"] = prefill_cpu_baseline(inp, acc, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def prefill_cpu_baseline(inp, acc, seconds: float):
+    """The float64 oracle (the non-absorbed definition) on whole (sequence,
+    head) pairs of the prefill: every query of one head of one prompt, which
+    materialises that head's keys and values once, as the prefill does.
+    value = the sample's share of the prefill's flops per second (all
+    prompts have one length, so a pair's share is 1 / (B * H))."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import mla_decode
+
+    c = inp.cfg
+    rng = np.random.default_rng(1)
+    pairs = [(int(rng.integers(0, c.batch)), int(rng.integers(0, c.heads))) for _ in range(64)]
+
+    def rows_of(ps):
+        return [(b, i, h) for b, h in ps for i in range(c.q_len)]
+
+    t1 = time.perf_counter()
+    mla_decode(inp, rows=rows_of(pairs[:1]))
+    per = max(time.perf_counter() - t1, 1e-3)
+    n = int(max(1, min(len(pairs), seconds / per)))
+    t1 = time.perf_counter()
+    mla_decode(inp, rows=rows_of(pairs[:n]))
+    dt = time.perf_counter() - t1
+    frac = n / (c.batch * c.heads)
+    blas = max([t.get("num_threads", 1) for t in threadpool_info()] or [1])
+    cores = len(os.sched_getaffinity(0))
+    return {"value": round(frac * (acc["expand_flops"] + acc["attn_flops"]) / dt / 1e12, 6),
+            "unit": "TFLOP/s", "cores": int(min(blas, cores)), "host_cpus": cores,
+            "os_cpu_count": os.cpu_count(), "blas_threads": int(blas), "kind": "oracle",
+            "sample": f"all {c.q_len} queries of {n} random (sequence, head) pairs of "
+                      f"{c.batch * c.heads}, {dt:.1f} s (includes the oracle's float64 "
+                      "conversion of its inputs); value = the sample's share of the prefill flops / time"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -205,10 +376,13 @@ def main():
         return
 
     import mla_latent_kv_lat_amd as mla
-    from mla_inputs import CONFIGS, HEADLINE, MLAInputs
+    from mla_inputs import CONFIGS, HEADLINE, PREFILL_CONFIGS, MLAInputs
     from mla_inputs.device import to_device
 
     name = args.workload or HEADLINE
+    if name in PREFILL_CONFIGS:
+        prefill_main(args, name, torch)
+        return
     cfg = CONFIGS[name]
     t0 = time.perf_counter()
     inp = MLAInputs(cfg)

@@ -52,6 +52,8 @@ def _compile(src: str) -> str:
 # sources the split-K decode kernel is built from (its measurements are tied to these)
 DECODE_SOURCES = ("decode_split.hip", "decode_common.hpp", "mfma_common.hpp", "common.hpp",
                   "kernels.hpp")
+PREFILL_SOURCES = ("prefill.hip", "decode_common.hpp", "mfma_common.hpp", "common.hpp",
+                   "kernels.hpp")
 
 
 def source_digest(files=None) -> str:
