@@ -43,6 +43,15 @@ namespace {
 using namespace mfma;
 using namespace dec;
 
+// Workgroups are dispatched to the 8 XCDs round-robin by linear id (id % 8).
+// Map id to an item so that XCD x gets the contiguous items
+// [x q + min(x, r), ...) of n = 8 q + r, in dispatch order: a bijection of
+// [0, n), since id = 8 k + x has k < q + (x < r).
+__device__ __forceinline__ uint32_t xcd_item(uint32_t id, uint32_t n) {
+  const uint32_t q = n >> 3, r = n & 7, x = id & 7;
+  return x * q + min(x, r) + (id >> 3);
+}
+
 // ------------------------------------------------------------------ expand
 
 constexpr int kExTok = 128;                  // tokens per workgroup
@@ -50,12 +59,14 @@ constexpr int kExKc = 64;                    // k per LDS chunk
 constexpr int kExOpBytes = 128 * kExKc * 2;  // 16 KB: one operand's chunk
 constexpr int kExBytes = 2 * 2 * kExOpBytes; // two buffers of A and B
 
-// 1 KB LDS block = 8 rows x 8 16-byte chunks; row rho, chunk kappa at entry
-// 8 rho + (kappa ^ rho), so a 32x32x16 operand read (32 rows, one chunk) and
-// the wave-wide fill (lane e -> row e/8, chunk (e%8) ^ row) are free of bank
-// conflicts.
+// 1 KB LDS block j = rows 8j..8j+7 x 8 16-byte chunks; row rho, chunk kappa
+// at entry 8 rho + (kappa ^ rho ^ (j & 1)).  A 32x32x16 operand read (32
+// rows, one chunk) is served 16 lanes at a time: rows 8j.. and 8(j+1).. of
+// one group then fall in complementary halves of the 64 banks.  The
+// wave-wide fill writes lane e at entry e, so it loads chunk
+// (e%8) ^ row ^ (j & 1).
 __device__ __forceinline__ uint32_t ex_entry(int row, int kap) {
-  return (uint32_t)((row >> 3) * 1024 + 16 * (8 * (row & 7) + (kap ^ (row & 7))));
+  return (uint32_t)((row >> 3) * 1024 + 16 * (8 * (row & 7) + (kap ^ (row & 7) ^ ((row >> 3) & 1))));
 }
 
 __global__ __launch_bounds__(256) void prefill_expand_kernel(PrefillArgs a) {
@@ -63,9 +74,18 @@ __global__ __launch_bounds__(256) void prefill_expand_kernel(PrefillArgs a) {
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int H = a.heads;
-  const int cb = blockIdx.x;                 // channel block: W_UK,h (cb < H) or W_UV,h
-  const int b = (int)(blockIdx.y / a.ntile);
-  const int t0 = (int)(blockIdx.y % a.ntile) * kExTok;
+  // Work order: workgroups reach the 8 XCDs round-robin by linear id, so
+  // XCD x is given the contiguous item range x*N/8.. (xcd_item).  Items run
+  // channel-block-fastest within groups of HG channel blocks, then token
+  // tiles, then groups: the workgroups an XCD runs at once share one token
+  // tile's latents and the group's HG x 128 KB of weights stay in its L2.
+  const uint32_t T = gridDim.y;
+  const uint32_t item = xcd_item(blockIdx.x + gridDim.x * blockIdx.y, gridDim.x * T);
+  const uint32_t HG = (2 * H) % 8 == 0 ? 8 : ((2 * H) % 4 == 0 ? 4 : 2);
+  const uint32_t rest = item / HG, tile = rest % T;
+  const int cb = (int)((rest / T) * HG + item % HG);  // channel block: W_UK,h (cb < H) or W_UV,h
+  const int b = (int)(tile / a.ntile);
+  const int t0 = (int)(tile % a.ntile) * kExTok;
   const int len = a.seq_lens[b];
   if (t0 >= len) return;  // uniform across the workgroup
   const bool is_v = cb >= H;
@@ -84,7 +104,7 @@ __global__ __launch_bounds__(256) void prefill_expand_kernel(PrefillArgs a) {
   const int64_t prow1 = t0 + kTile < len ? page_row(pg0 + 1) : prow0;
 
   // fill lane: row e/8 of a block, chunk (e%8) ^ row
-  const int frow = lane >> 3, fkap = (lane & 7) ^ frow;
+  const int frow = lane >> 3, fkap = (lane & 7) ^ frow ^ (w & 1);
   // block j of a chunk: j < 16 the tokens' latents (rows 8j..), else the
   // weight rows 8(j-16)..; wave w issues j = w, w+4, .., w+28
   auto issue = [&](int kc, int buf) {
@@ -186,8 +206,13 @@ __global__ __launch_bounds__(1024) void prefill_attn_kernel(PrefillArgs a) {
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int H = a.heads, Lq = a.q_len;
   const int nqb = (Lq + kAtRows - 1) / kAtRows;
-  const int qb = nqb - 1 - (int)blockIdx.x;  // the longest causal ranges first
-  const int h = blockIdx.y, b = blockIdx.z;
+  // each XCD runs a contiguous range of (sequence, head, query block) items
+  // (xcd_item), so the query blocks of one head, which read the same keys
+  // and values, share an L2
+  const uint32_t item = xcd_item(blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z),
+                                 gridDim.x * gridDim.y * gridDim.z);
+  const int qb = nqb - 1 - (int)(item % (uint32_t)nqb);  // the longest causal ranges first
+  const int h = (int)((item / (uint32_t)nqb) % (uint32_t)H), b = (int)(item / ((uint32_t)nqb * (uint32_t)H));
   const int len = a.seq_lens[b];
   const int i0 = qb * kAtRows;
   const int64_t Tmax = a.max_seq_len;
@@ -205,6 +230,13 @@ __global__ __launch_bounds__(1024) void prefill_attn_kernel(PrefillArgs a) {
   const bool active = wrow0 < Lq;  // uniform per wave
   const int wave_vis = active ? min(len, max(0, n_vis(min(wrow0 + 15, Lq - 1)))) : 0;
 
+  // ---- RoPE frequencies base^(-2p/64) of the 32 pairs, once per workgroup
+  // (in the first ring slot, which the fills overwrite only later)
+  const double* theta = (const double*)smem;
+  if (threadIdx.x < 32)
+    ((double*)smem)[threadIdx.x] = exp2(-2.0 * (int)threadIdx.x / 64.0 * log2((double)a.rope_base));
+  block_sync();
+
   // ---- the wave's query rows: q_nope in k-slices 0-3, RoPE(q_rope) in 4-5
   bf16x8 q[6];
   {
@@ -216,7 +248,6 @@ __global__ __launch_bounds__(1024) void prefill_attn_kernel(PrefillArgs a) {
     for (int kk = 0; kk < 4; ++kk) q[kk] = qn[4 * kk + g];
     const bf16x8* qr = (const bf16x8*)((const uint16_t*)a.q_rope + qrow * 64);
     const double pos = (double)a.positions[(int64_t)b * Lq + i];
-    const double l2b = log2((double)a.rope_base);
 #pragma unroll
     for (int kk = 4; kk < 6; ++kk) {
       const bf16x8 x = qr[4 * (kk - 4) + g];
@@ -226,7 +257,7 @@ __global__ __launch_bounds__(1024) void prefill_attn_kernel(PrefillArgs a) {
         // pair p = 16 (kk-4) + 4 g + m turns by pos * base^(-2p/64); the
         // angle is reduced modulo 2 pi in double, sin/cos in single
         const int p = 16 * (kk - 4) + 4 * g + m;
-        double ang = pos * exp2(-2.0 * p / 64.0 * l2b);
+        double ang = pos * theta[p];
         ang -= 6.283185307179586 * rint(ang * 0.15915494309189535);
         float sn, cs;
         __sincosf((float)ang, &sn, &cs);
@@ -411,7 +442,9 @@ bool prefill_supports(const mla_dims_t& d, int64_t row_stride, int max_seq_len) 
   return d.q_dtype == MLA_BF16 && d.kv_dtype == MLA_BF16 && d.d_nope == 128 && d.d_v == 128 &&
          d.d_rope == 64 && d.d_latent == 512 && row_stride % 8 == 0 && row_stride <= (1 << 16) &&
          (int64_t)d.heads * 256 * 32 < ((int64_t)1 << 31) && max_seq_len <= kAtMaxPages * kTile &&
-         (int64_t)d.batch * ((max_seq_len + kExTok - 1) / kExTok) <= 65535 && d.heads <= 32767;
+         (int64_t)d.batch * ((max_seq_len + kExTok - 1) / kExTok) <= 65535 && d.heads <= 32767 &&
+         // the work-order maps index all workgroups of a launch in 32 bits
+         (int64_t)d.batch * d.heads * ((d.q_len + kAtRows - 1) / kAtRows) < ((int64_t)1 << 31);
 }
 
 hipError_t launch_prefill_expand(const mla_dims_t& d, const PrefillArgs& a, hipStream_t s) {
