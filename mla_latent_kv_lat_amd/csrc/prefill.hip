@@ -32,6 +32,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "common.hpp"
 #include "decode_common.hpp"
 #include "kernels.hpp"
@@ -197,7 +199,9 @@ constexpr int kAtKBytes = 3 * kAtCg;            // 24 KB: keys, column groups 0-
 constexpr int kAtSubBytes = kAtKBytes + 2 * kAtCg;  // + 16 KB values
 constexpr int kAtRing = 3;
 constexpr int kAtMaxPages = 4096;               // 262144 tokens
-constexpr int kAtBytes = kAtRing * kAtSubBytes + kAtMaxPages * 4;
+constexpr int kAtPageOff = kAtRing * kAtSubBytes;
+constexpr int kAtThetaOff = kAtPageOff + kAtMaxPages * 4;
+constexpr int kAtBytes = kAtThetaOff + 32 * 8;
 static_assert(kAtBytes <= 163840, "LDS budget");
 
 __global__ __launch_bounds__(1024) void prefill_attn_kernel(PrefillArgs a) {
@@ -206,18 +210,37 @@ __global__ __launch_bounds__(1024) void prefill_attn_kernel(PrefillArgs a) {
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int H = a.heads, Lq = a.q_len;
   const int nqb = (Lq + kAtRows - 1) / kAtRows;
-  // each XCD runs a contiguous range of (sequence, head, query block) items
-  // (xcd_item), so the query blocks of one head, which read the same keys
-  // and values, share an L2
-  const uint32_t item = xcd_item(blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z),
-                                 gridDim.x * gridDim.y * gridDim.z);
-  const int qb = nqb - 1 - (int)(item % (uint32_t)nqb);  // the longest causal ranges first
+  const int64_t Tmax = a.max_seq_len;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_char*)smem;
+  int* prow = (int*)(smem + kAtPageOff);  // block id (paged) of each page of the item
+
+  // RoPE frequencies base^(-2p/64) of the 32 pairs, once (the first
+  // item's barrier orders them before use)
+  double* theta = (double*)(smem + kAtThetaOff);
+  if (threadIdx.x < 32) theta[threadIdx.x] = exp2(-2.0 * (int)threadIdx.x / 64.0 * log2((double)a.rope_base));
+
+  // Persistent workgroups, one per compute unit: the items, (sequence,
+  // head, query block) with the query blocks of a head consecutive and the
+  // longest causal range first, are cut into P = min(8, grid) contiguous
+  // ranges; workgroup g takes range g % P, which is its XCD's when the
+  // grid is a multiple of 8 (workgroups reach the XCDs round-robin), so
+  // the query blocks of one head share an L2.  Its nx workgroups deal the
+  // range out in rounds of nx items, the order reversed every other round
+  // so that the long and short blocks of the heads even out.
+  const uint32_t n_items = (uint32_t)nqb * (uint32_t)H * (uint32_t)a.batch;
+  const uint32_t G = gridDim.x, g = blockIdx.x;
+  const uint32_t P = G < 8 ? G : 8, pi = g % P, rank = g / P, nx = (G - pi + P - 1) / P;
+  const uint32_t cnt = n_items / P + (pi < n_items % P ? 1u : 0u);
+  const uint32_t beg = pi * (n_items / P) + min(pi, n_items % P);
+
+  for (uint32_t rd = 0;; ++rd) {
+  const uint32_t loc = rd * nx + ((rd & 1) ? nx - 1 - rank : rank);
+  if (loc >= cnt) break;  // uniform
+  const uint32_t item = beg + loc;
+  const int qb = nqb - 1 - (int)(item % (uint32_t)nqb);
   const int h = (int)((item / (uint32_t)nqb) % (uint32_t)H), b = (int)(item / ((uint32_t)nqb * (uint32_t)H));
   const int len = a.seq_lens[b];
   const int i0 = qb * kAtRows;
-  const int64_t Tmax = a.max_seq_len;
-  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_char*)smem;
-  int* prow = (int*)(smem + kAtRing * kAtSubBytes);  // block id (paged) of each page
 
   // visible tokens of query i: t < len - Lq + i + 1 (causal) or t < len
   auto n_vis = [&](int i) { return a.causal ? len - Lq + i + 1 : len; };
@@ -230,52 +253,12 @@ __global__ __launch_bounds__(1024) void prefill_attn_kernel(PrefillArgs a) {
   const bool active = wrow0 < Lq;  // uniform per wave
   const int wave_vis = active ? min(len, max(0, n_vis(min(wrow0 + 15, Lq - 1)))) : 0;
 
-  // ---- RoPE frequencies base^(-2p/64) of the 32 pairs, once per workgroup
-  // (in the first ring slot, which the fills overwrite only later)
-  const double* theta = (const double*)smem;
-  if (threadIdx.x < 32)
-    ((double*)smem)[threadIdx.x] = exp2(-2.0 * (int)threadIdx.x / 64.0 * log2((double)a.rope_base));
-  block_sync();
-
-  // ---- the wave's query rows: q_nope in k-slices 0-3, RoPE(q_rope) in 4-5
-  bf16x8 q[6];
-  {
-    const int li = lane & 15, g = lane >> 4;
-    const int i = min(wrow0 + li, Lq - 1);
-    const int64_t qrow = ((int64_t)b * Lq + i) * H + h;
-    const bf16x8* qn = (const bf16x8*)((const uint16_t*)a.q_nope + qrow * 128);
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) q[kk] = qn[4 * kk + g];
-    const bf16x8* qr = (const bf16x8*)((const uint16_t*)a.q_rope + qrow * 64);
-    const double pos = (double)a.positions[(int64_t)b * Lq + i];
-#pragma unroll
-    for (int kk = 4; kk < 6; ++kk) {
-      const bf16x8 x = qr[4 * (kk - 4) + g];
-      bf16x8 y;
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        // pair p = 16 (kk-4) + 4 g + m turns by pos * base^(-2p/64); the
-        // angle is reduced modulo 2 pi in double, sin/cos in single
-        const int p = 16 * (kk - 4) + 4 * g + m;
-        double ang = pos * theta[p];
-        ang -= 6.283185307179586 * rint(ang * 0.15915494309189535);
-        float sn, cs;
-        __sincosf((float)ang, &sn, &cs);
-        const float x0 = (float)x[2 * m], x1 = (float)x[2 * m + 1];
-        y[2 * m] = (__bf16)(x0 * cs - x1 * sn);
-        y[2 * m + 1] = (__bf16)(x0 * sn + x1 * cs);
-      }
-      q[kk] = y;
-    }
-#pragma unroll
-    for (int kk = 0; kk < 6; ++kk) asm volatile("" ::"v"(q[kk]));  // loaded before the fills go out
-  }
-  // page table of the tokens this workgroup reads
+  // page table of the tokens this item reads; the barrier also ends the
+  // previous item's use of the ring
   if (a.block_table) {
     const int npg = (n_end + kTile - 1) / kTile;
-    for (int p = (int)threadIdx.x; p < npg; p += 1024) prow[p] = a.block_table[(int64_t)b * a.mbps + p];
+    for (int pg = (int)threadIdx.x; pg < npg; pg += 1024) prow[pg] = a.block_table[(int64_t)b * a.mbps + pg];
   }
-  wait_vm0();
   block_sync();
 
   // ---- fills: 40 blocks of 1 KB per sub-tile (keys: column groups 0-1
@@ -283,10 +266,13 @@ __global__ __launch_bounds__(1024) void prefill_attn_kernel(PrefillArgs a) {
   // wave k % 16; all of a wave's blocks are row group w & 7
   const int n_share = w < 8 ? 3 : 2;
   const int rg = w & 7;
-  const int kap = (lane >> 3) ^ (rg & 1);
-  const int rho = (lane & 7) ^ (4 * ((kap ^ (kap >> 1)) & 1));
   int pz = 0;  // next sub-tile to fill
   auto issue = [&]() {
+    // lane offsets from an opaque lane id: recomputed here, not kept live
+    // across the item loop
+    const int fl = fresh_lane();
+    const int kap = (fl >> 3) ^ (rg & 1);
+    const int rho = (fl & 7) ^ (4 * ((kap ^ (kap >> 1)) & 1));
     const int t0 = pz * kAtSub;
     const uint32_t slot = lds0 + (uint32_t)((pz % kAtRing) * kAtSubBytes);
     const int tl = min(t0 + 8 * rg + rho, len - 1) - t0;  // clamped rows are masked
@@ -298,18 +284,59 @@ __global__ __launch_bounds__(1024) void prefill_attn_kernel(PrefillArgs a) {
         const int cg = (k < 16 ? k : k - 24) >> 3;
         const char* base = (const char*)(k < 16 ? a.k_nope : a.v) + (((int64_t)b * Tmax + t0) * H + h) * 256;
         const uint32_t voff = (uint32_t)(tl * H * 256) + (uint32_t)((cg * 64 + kap * 8) * 2);
-        lds_dma16_stream(base, voff, slot + (uint32_t)((k < 16 ? 0 : kAtKBytes) + cg * kAtCg + rg * 1024));
+        lds_dma16_stream((const char*)uniform64((int64_t)base), voff,
+                         __builtin_amdgcn_readfirstlane(slot + (uint32_t)((k < 16 ? 0 : kAtKBytes) + cg * kAtCg + rg * 1024)));
       } else {  // RoPE key of the cache rows (the sub-tile is one page)
         const int64_t r0 = a.block_table ? (int64_t)prow[t0 >> 6] * kTile : (int64_t)b * Tmax + t0;
         const char* base = (const char*)a.rope + r0 * a.row_stride * 2;
         const uint32_t voff = (uint32_t)(tl * a.row_stride * 2) + (uint32_t)(kap * 16);
-        lds_dma16_stream(base, voff, slot + (uint32_t)(2 * kAtCg + rg * 1024));
+        lds_dma16_stream((const char*)uniform64((int64_t)base), voff,
+                         __builtin_amdgcn_readfirstlane(slot + (uint32_t)(2 * kAtCg + rg * 1024)));
       }
     }
     ++pz;
   };
 
+  // the first sub-tiles go out before the query loads, so both latencies
+  // overlap
   for (int z = 0; z < kAtRing - 1 && z < nsub; ++z) issue();
+
+  // ---- the wave's query rows: q_nope in k-slices 0-3, RoPE(q_rope) in 4-5
+  bf16x8 q[6];
+  {
+    const int fl = fresh_lane();
+    const int li = fl & 15, gq = fl >> 4;
+    const int i = min(wrow0 + li, Lq - 1);
+    const int64_t qrow = ((int64_t)b * Lq + i) * H + h;
+    const bf16x8* qn = (const bf16x8*)((const uint16_t*)a.q_nope + qrow * 128);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) q[kk] = qn[4 * kk + gq];
+    const bf16x8* qr = (const bf16x8*)((const uint16_t*)a.q_rope + qrow * 64);
+    const double pos = (double)a.positions[(int64_t)b * Lq + i];
+#pragma unroll
+    for (int kk = 4; kk < 6; ++kk) {
+      const bf16x8 x = qr[4 * (kk - 4) + gq];
+      bf16x8 y;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        // pair p = 16 (kk-4) + 4 gq + m turns by pos * base^(-2p/64); the
+        // angle is reduced modulo 2 pi in double, sin/cos in single
+        const int pr = 16 * (kk - 4) + 4 * gq + m;
+        double ang = pos * theta[pr];
+        ang -= 6.283185307179586 * rint(ang * 0.15915494309189535);
+        float sn, cs;
+        __sincosf((float)ang, &sn, &cs);
+        const float x0 = (float)x[2 * m], x1 = (float)x[2 * m + 1];
+        y[2 * m] = (__bf16)(x0 * cs - x1 * sn);
+        y[2 * m + 1] = (__bf16)(x0 * sn + x1 * cs);
+      }
+      q[kk] = y;
+    }
+    // taken here: the compiler's waits for the query (it does not count
+    // the direct loads issued before them) then also cover sub-tiles 0-1
+#pragma unroll
+    for (int kk = 0; kk < 6; ++kk) asm volatile("" ::"v"(q[kk]));
+  }
   if (nsub > 0) wait_vm(n_share * (pz - 1));
   block_sync();
 
@@ -429,14 +456,27 @@ __global__ __launch_bounds__(1024) void prefill_attn_kernel(PrefillArgs a) {
     uint16_t* orow = (uint16_t*)a.o + row * 128 + 4 * (lw >> 4);
 #pragma unroll
     for (int nb = 0; nb < 8; ++nb) {
-      const uint2 v2 = make_uint2((uint32_t)f32_to_bf16(o[nb][0] * inv) | ((uint32_t)f32_to_bf16(o[nb][1] * inv) << 16),
-                                  (uint32_t)f32_to_bf16(o[nb][2] * inv) | ((uint32_t)f32_to_bf16(o[nb][3] * inv) << 16));
-      *(uint2*)(orow + 16 * nb) = v2;
+      const bf16x4 v4 = {(__bf16)(o[nb][0] * inv), (__bf16)(o[nb][1] * inv), (__bf16)(o[nb][2] * inv),
+                         (__bf16)(o[nb][3] * inv)};
+      *(bf16x4*)(orow + 16 * nb) = v4;
     }
   }
+  }  // items
 }
 
 }  // namespace
+
+// compute units of the current device, looked up once per device
+static int cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+  cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
 
 bool prefill_supports(const mla_dims_t& d, int64_t row_stride, int max_seq_len) {
   return d.q_dtype == MLA_BF16 && d.kv_dtype == MLA_BF16 && d.d_nope == 128 && d.d_v == 128 &&
@@ -456,8 +496,12 @@ hipError_t launch_prefill_expand(const mla_dims_t& d, const PrefillArgs& a, hipS
 }
 
 hipError_t launch_prefill_attn(const mla_dims_t& d, const PrefillArgs& a, hipStream_t s) {
-  dim3 grid((unsigned)((d.q_len + kAtRows - 1) / kAtRows), (unsigned)d.heads, (unsigned)d.batch);
-  hipLaunchKernelGGL(prefill_attn_kernel, grid, dim3(1024), 0, s, a);
+  // one persistent workgroup per compute unit (fewer when there are fewer items)
+  const int64_t items = (int64_t)((d.q_len + kAtRows - 1) / kAtRows) * d.heads * d.batch;
+  const int64_t cus = cu_count();
+  const unsigned grid = (unsigned)(items < cus ? items : cus);
+  if (grid == 0) return hipSuccess;
+  hipLaunchKernelGGL(prefill_attn_kernel, dim3(grid), dim3(1024), 0, s, a);
   return hipGetLastError();
 }
 
