@@ -14,17 +14,19 @@
 //
 // prefill_expand_kernel: k_nope[b,t,h,:] = W_UK,h c_t and v[b,t,h,:] = W_UV,h c_t
 //   for every cached token, one GEMM of the tokens' latents (K = 512) against
-//   the 2H x 128 rows of W_UK and W_UV.  Workgroup = 128 tokens of one
-//   sequence x one head's 128 k or v channels, 4 waves of 64 x 64 on
-//   v_mfma_f32_32x32x16_bf16; both operands stream through LDS in 64-wide k
-//   chunks (direct global->LDS loads, double buffered).
+//   the 2H x 128 rows of W_UK and W_UV.  Workgroup = 256 tokens of one
+//   sequence x one head's 256 k and v channels, 16 waves of 64 x 64 on
+//   v_mfma_f32_32x32x16_bf16; both operands stream through a 4-stage LDS
+//   ring in 32-wide k chunks (direct global->LDS loads), and the outputs
+//   leave through LDS as whole 256-byte rows.
 //
 // prefill_attn_kernel: causal attention of the Lq prompt tokens of each
 //   sequence over its keys [k_nope ; k_rope] (192 wide, the decoupled RoPE
-//   key shared by the heads) and values (128 wide).  Workgroup = 256 query
-//   rows of one (sequence, head), 16 waves of 16 rows; the keys and values of
-//   64 tokens (one page) at a time are filled into LDS once for all 256 rows.  Each wave
-//   computes S^T = K Q^T, the online softmax and O^T += V^T P^T on
+//   key shared by the heads) and values (128 wide).  Persistent workgroups
+//   (one per compute unit) take items of 256 query rows of one (sequence,
+//   head), 16 waves of 16 rows; the keys and values of 64 tokens (one page)
+//   at a time are filled into LDS once for all 256 rows.  Each wave computes
+//   S^T = K Q^T, the online softmax and O^T += V^T P^T on
 //   v_mfma_f32_16x16x32_bf16 with P fed from the score registers, exactly as
 //   the decode kernel does with the latent (same LDS layout and operand
 //   addressing).
@@ -56,137 +58,159 @@ __device__ __forceinline__ uint32_t xcd_item(uint32_t id, uint32_t n) {
 
 // ------------------------------------------------------------------ expand
 
-constexpr int kExTok = 128;                  // tokens per workgroup
-constexpr int kExKc = 64;                    // k per LDS chunk
-constexpr int kExOpBytes = 128 * kExKc * 2;  // 16 KB: one operand's chunk
-constexpr int kExBytes = 2 * 2 * kExOpBytes; // two buffers of A and B
+constexpr int kExTok = 256;                  // tokens per workgroup (four pages)
+constexpr int kExCh = 256;                   // output channels: one head's k_nope and v
+constexpr int kExKc = 32;                    // k per LDS chunk
+constexpr int kExOpBytes = 256 * kExKc * 2;  // 16 KB: one operand's chunk
+constexpr int kExStage = 2 * kExOpBytes;     // weights then latents
+constexpr int kExRing = 4;                   // chunks kc .. kc+3
+constexpr int kExPitch = 528;                // bytes per token row of the staged outputs
+constexpr int kExBytes = kExTok * kExPitch > kExRing * kExStage ? kExTok * kExPitch : kExRing * kExStage;
+static_assert(kExBytes <= 163840, "LDS budget");
 
-// 1 KB LDS block j = rows 8j..8j+7 x 8 16-byte chunks; row rho, chunk kappa
-// at entry 8 rho + (kappa ^ rho ^ (j & 1)).  A 32x32x16 operand read (32
-// rows, one chunk) is served 16 lanes at a time: rows 8j.. and 8(j+1).. of
-// one group then fall in complementary halves of the 64 banks.  The
-// wave-wide fill writes lane e at entry e, so it loads chunk
-// (e%8) ^ row ^ (j & 1).
+// 1 KB LDS block j = rows 16j..16j+15 of 64 bytes (four 16-byte chunks of
+// 8 k); row rho, chunk kappa at entry 4 rho + (kappa ^ ((rho >> 2) & 3)).
+// A 32x32x16 operand read (one chunk of 32 rows) is served 16 lanes at a
+// time; rows 4m..4m+3 fill the 64 banks once each.  The wave-wide fill
+// writes lane e at entry e, so it loads chunk (e%4) ^ ((e/16) & 3).
 __device__ __forceinline__ uint32_t ex_entry(int row, int kap) {
-  return (uint32_t)((row >> 3) * 1024 + 16 * (8 * (row & 7) + (kap ^ (row & 7) ^ ((row >> 3) & 1))));
+  return (uint32_t)(row * 64 + 16 * (kap ^ ((row >> 2) & 3)));
 }
 
-__global__ __launch_bounds__(256) void prefill_expand_kernel(PrefillArgs a) {
+// One GEMM per (sequence, 256-token tile, head): C^T = [W_UK,h ; W_UV,h] X^T
+// with X the tiles' cached latents (K = 512).  16 waves of 64 channels x 64
+// tokens on v_mfma_f32_32x32x16_bf16; the outputs are staged in LDS as
+// bf16 token rows and leave as 16-byte row pieces.
+__global__ __launch_bounds__(1024) void prefill_expand_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem[kExBytes];
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int H = a.heads;
   // Work order: workgroups reach the 8 XCDs round-robin by linear id, so
   // XCD x is given the contiguous item range x*N/8.. (xcd_item).  Items run
-  // channel-block-fastest within groups of HG channel blocks, then token
-  // tiles, then groups: the workgroups an XCD runs at once share one token
-  // tile's latents and the group's HG x 128 KB of weights stay in its L2.
-  const uint32_t T = gridDim.y;
-  const uint32_t item = xcd_item(blockIdx.x + gridDim.x * blockIdx.y, gridDim.x * T);
-  const uint32_t HG = (2 * H) % 8 == 0 ? 8 : ((2 * H) % 4 == 0 ? 4 : 2);
+  // head-fastest within groups of HG heads, then token tiles, then groups:
+  // the workgroups an XCD runs at once share a few token tiles' latents and
+  // the group's HG x 256 KB of weights stay in its L2.
+  const uint32_t T = (uint32_t)a.batch * (uint32_t)a.ntile;
+  const uint32_t item = xcd_item(blockIdx.x, gridDim.x);
+  const uint32_t HG = H % 8 == 0 ? 8 : (H % 4 == 0 ? 4 : (H % 2 == 0 ? 2 : 1));
   const uint32_t rest = item / HG, tile = rest % T;
-  const int cb = (int)((rest / T) * HG + item % HG);  // channel block: W_UK,h (cb < H) or W_UV,h
+  const int h = (int)((rest / T) * HG + item % HG);
   const int b = (int)(tile / a.ntile);
   const int t0 = (int)(tile % a.ntile) * kExTok;
   const int len = a.seq_lens[b];
   if (t0 >= len) return;  // uniform across the workgroup
-  const bool is_v = cb >= H;
-  const int h = is_v ? cb - H : cb;
-  const uint16_t* wsrc = (is_v ? a.w_uv : a.w_uk) + (int64_t)h * 128 * 512;
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_char*)smem;
 
-  // first cache row of the tile's two 64-token pages (the second only when
-  // the sequence reaches it)
-  auto page_row = [&](int page) -> int64_t {
-    return a.block_table ? (int64_t)a.block_table[(int64_t)b * a.mbps + page] * kTile
-                         : (int64_t)b * a.max_seq_len + (int64_t)page * kTile;
-  };
-  const int pg0 = t0 >> 6;
-  const int64_t prow0 = page_row(pg0);
-  const int64_t prow1 = t0 + kTile < len ? page_row(pg0 + 1) : prow0;
-
-  // fill lane: row e/8 of a block, chunk (e%8) ^ row
-  const int frow = lane >> 3, fkap = (lane & 7) ^ frow ^ (w & 1);
-  // block j of a chunk: j < 16 the tokens' latents (rows 8j..), else the
-  // weight rows 8(j-16)..; wave w issues j = w, w+4, .., w+28
-  auto issue = [&](int kc, int buf) {
-    const uint32_t dst = lds0 + (uint32_t)(buf * 2 * kExOpBytes);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int j = w + 4 * i;
-      if (j < 16) {
-        // the block's rows, clamped to the sequence's last token (a whole
-        // block past the end re-reads it); all in one page
-        const int tb = min(t0 + 8 * j, len - 1);
-        const int ps = tb & ~(kTile - 1);
-        const int64_t r0 = (tb >> 6) == pg0 ? prow0 : prow1;
-        const int tl = min(t0 + 8 * j + frow, len - 1) - ps;
-        const char* base = (const char*)a.latent + r0 * a.row_stride * 2;
-        const uint32_t voff = (uint32_t)(tl * a.row_stride * 2) + (uint32_t)((kc * kExKc + fkap * 8) * 2);
-        lds_dma16(base, voff, dst + (uint32_t)(j * 1024));
-      } else {
-        const int jr = j - 16;
-        const uint32_t voff = (uint32_t)(((8 * jr + frow) * 512 + kc * kExKc + fkap * 8) * 2);
-        lds_dma16(wsrc, voff, dst + (uint32_t)(kExOpBytes + jr * 1024));
-      }
-    }
+  // fills: per chunk, wave w loads weight rows 16w.. (block w) and token
+  // rows 16w.. (block w); the token block lies in one page
+  const int fr = lane >> 2;                       // row in the block
+  const int fk = (lane & 3) ^ ((lane >> 4) & 3);  // chunk this lane loads
+  // weight rows 16w.. = output channels: W_UK,h rows for w < 8, W_UV,h after
+  const uint16_t* wsrc = (w < 8 ? a.w_uk : a.w_uv) + ((int64_t)h * 128 + ((16 * w) & 127)) * 512;
+  const int tb = min(t0 + 16 * w, len - 1);       // the block's rows, clamped to the last token
+  const int64_t prow = a.block_table ? (int64_t)a.block_table[(int64_t)b * a.mbps + (tb >> 6)] * kTile
+                                     : (int64_t)b * a.max_seq_len + (tb & ~(kTile - 1));
+  const int tl = min(t0 + 16 * w + fr, len - 1) - (tb & ~(kTile - 1));
+  const char* xbase = (const char*)a.latent + prow * a.row_stride * 2;
+  const uint32_t xoff = (uint32_t)(tl * a.row_stride * 2) + (uint32_t)(fk * 16);
+  const uint32_t woff = (uint32_t)(fr * 1024 + fk * 16);
+  auto issue = [&](int kc) {
+    const uint32_t dst = lds0 + (uint32_t)((kc % kExRing) * kExStage + w * 1024);
+    lds_dma16((const char*)wsrc, woff + (uint32_t)(kc * kExKc * 2), dst);
+    lds_dma16((const char*)uniform64((int64_t)xbase), xoff + (uint32_t)(kc * kExKc * 2), dst + kExOpBytes);
   };
 
-  const int wr = w >> 1, wc = w & 1;  // wave tile: tokens 64 wr.., channels 64 wc..
+  const int wch = w & 3, wtk = w >> 2;  // wave tile: channels 64 wch.., tokens 64 wtk..
   f32x16 acc[2][2];
 #pragma unroll
   for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
     for (int ni = 0; ni < 2; ++ni) acc[mi][ni] = f32x16{};
 
-  issue(0, 0);
+  // operands of k-step half kh (16 k) of chunk kc
+  auto kread = [&](int kc, int kh, bf16x8 (&wv)[2], bf16x8 (&xv)[2]) {
+    const char* Wm = smem + (kc % kExRing) * kExStage;
+    const char* Xm = Wm + kExOpBytes;
+    const int lr = fresh_lane();
+    const int l32 = lr & 31, kap = 2 * kh + (lr >> 5);
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi) wv[mi] = *(const bf16x8*)(Wm + ex_entry(64 * wch + 32 * mi + l32, kap));
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni) xv[ni] = *(const bf16x8*)(Xm + ex_entry(64 * wtk + 32 * ni + l32, kap));
+  };
+  auto kmul = [&](const bf16x8 (&wv)[2], const bf16x8 (&xv)[2]) {
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni) acc[mi][ni] = mfma32(wv[mi], xv[ni], acc[mi][ni]);
+  };
+
+  // The operands of the next k-step are read while the current one
+  // multiplies; a chunk's barrier comes right after its predecessor's last
+  // products are issued, so the matrix cores stay busy across it.  After
+  // the barrier for chunk m every wave has read chunk m-1 into registers,
+  // and chunk m+3 goes into its stage.
   constexpr int kChunks = 512 / kExKc;
+#pragma unroll
+  for (int kc = 0; kc < kExRing; ++kc) issue(kc);
+  wait_vm(2 * (kExRing - 1));  // this wave's loads of chunk 0 landed
+  block_sync();
+  bf16x8 cw[2], cx[2], nw[2], nx[2];
+  kread(0, 0, cw, cx);
   for (int kc = 0; kc < kChunks; ++kc) {
-    if (kc + 1 < kChunks) issue(kc + 1, (kc + 1) & 1);
-    if (kc + 1 < kChunks)
-      wait_vm(8);  // this wave's loads of chunk kc landed (those of kc+1 in flight)
-    else
-      wait_vm(0);
-    block_sync();
-    const char* A = smem + (kc & 1) * 2 * kExOpBytes;
-    const char* Bm = A + kExOpBytes;
-    const int l32 = lane & 31, hk = lane >> 5;
-#pragma unroll
-    for (int ks = 0; ks < kExKc / 16; ++ks) {
-      const int kap = 2 * ks + hk;
-      bf16x8 av[2], bv[2];
-#pragma unroll
-      for (int mi = 0; mi < 2; ++mi)
-        av[mi] = *(const bf16x8*)(A + ex_entry(64 * wr + 32 * mi + l32, kap));
-#pragma unroll
-      for (int ni = 0; ni < 2; ++ni)
-        bv[ni] = *(const bf16x8*)(Bm + ex_entry(64 * wc + 32 * ni + l32, kap));
-#pragma unroll
-      for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < 2; ++ni) acc[mi][ni] = mfma32(av[mi], bv[ni], acc[mi][ni]);
+    kread(kc, 1, nw, nx);
+    kmul(cw, cx);
+    // chunk kc+3 into the stage of kc-1 (read by everyone before the last
+    // barrier); issued once products are queued, so that the wait for a
+    // free slot in the load queue overlaps them
+    __builtin_amdgcn_sched_barrier(0);
+    if (kc >= 1 && kc + kExRing - 1 < kChunks) issue(kc + kExRing - 1);
+    kmul(nw, nx);
+    __builtin_amdgcn_sched_barrier(0);  // the products go out before the wait and the barrier
+    if (kc + 1 < kChunks) {
+      const int m = kc + 1;
+      const int later = min(2, kChunks - 1 - m);  // chunks after m already issued
+      if (later == 2) wait_vm(4); else if (later == 1) wait_vm(2); else wait_vm(0);
+      block_sync();  // chunk m complete for everyone; chunk m-1 read by everyone
+      kread(m, 0, cw, cx);
     }
-    block_sync();  // the buffer is refilled by the loads of chunk kc+2
   }
 #pragma unroll
   for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
     for (int ni = 0; ni < 2; ++ni) mfma_settle(acc[mi][ni]);
+  block_sync();  // every wave's last operand reads done: the ring becomes the staging area
 
-  // C (32 x 32): lane l holds channel l%32, tokens 8(r/4) + 4(l/32) + r%4
-  uint16_t* dst = (uint16_t*)(is_v ? a.v : a.k_nope);
-  const int ch = lane & 31, hr = lane >> 5;
+  // C^T (32 x 32): lane l holds token l%32 and channels 8(r/4) + 4(l/32) + r%4
+  {
+    const int ls = fresh_lane();
 #pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
+    for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int t = t0 + 64 * wr + 32 * mi + 8 * (r >> 2) + 4 * hr + (r & 3);
-      if (t < len) {
-        uint16_t* row = dst + (((int64_t)b * a.max_seq_len + t) * H + h) * 128 + 64 * wc + ch;
-        row[0] = f32_to_bf16(acc[mi][0][r]);
-        row[32] = f32_to_bf16(acc[mi][1][r]);
-      }
+      for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int tok = 64 * wtk + 32 * ni + (ls & 31);
+          const int ch = 64 * wch + 32 * mi + 8 * g4 + 4 * (ls >> 5);
+          const bf16x4 v4 = {(__bf16)acc[mi][ni][4 * g4], (__bf16)acc[mi][ni][4 * g4 + 1],
+                             (__bf16)acc[mi][ni][4 * g4 + 2], (__bf16)acc[mi][ni][4 * g4 + 3]};
+          *(bf16x4*)(smem + tok * kExPitch + ch * 2) = v4;
+        }
+  }
+  block_sync();
+  // token rows out: 32 pieces of 16 bytes per token (16 of k_nope, 16 of v)
+  const int64_t T2 = a.max_seq_len;
+#pragma unroll
+  for (int j = 0; j < kExTok * 32 / 1024; ++j) {
+    const int e = (int)threadIdx.x + 1024 * j;
+    const int tk = e >> 5, cc = e & 31;
+    if (t0 + tk < len) {
+      const uint4 v = *(const uint4*)(smem + tk * kExPitch + cc * 16);
+      char* dst = (char*)(cc < 16 ? a.k_nope : a.v) + (((int64_t)b * T2 + t0 + tk) * H + h) * 256 + (cc & 15) * 16;
+      *(uint4*)dst = v;
     }
+  }
 }
 
 // --------------------------------------------------------------- attention
@@ -219,26 +243,31 @@ __global__ __launch_bounds__(1024) void prefill_attn_kernel(PrefillArgs a) {
   double* theta = (double*)(smem + kAtThetaOff);
   if (threadIdx.x < 32) theta[threadIdx.x] = exp2(-2.0 * (int)threadIdx.x / 64.0 * log2((double)a.rope_base));
 
-  // Persistent workgroups, one per compute unit: the items, (sequence,
-  // head, query block) with the query blocks of a head consecutive and the
-  // longest causal range first, are cut into P = min(8, grid) contiguous
-  // ranges; workgroup g takes range g % P, which is its XCD's when the
-  // grid is a multiple of 8 (workgroups reach the XCDs round-robin), so
-  // the query blocks of one head share an L2.  Its nx workgroups deal the
-  // range out in rounds of nx items, the order reversed every other round
-  // so that the long and short blocks of the heads even out.
-  const uint32_t n_items = (uint32_t)nqb * (uint32_t)H * (uint32_t)a.batch;
+  // Persistent workgroups, one per compute unit.  An item is a pair of
+  // query blocks of one (sequence, head), p and nqb-1-p, whose causal
+  // ranges add up to the same length for every p, so all items cost the
+  // same when the sequences do.  The items, those of a head consecutive,
+  // are cut into P = min(8, grid) contiguous ranges; workgroup g takes
+  // range g % P, which is its XCD's when the grid is a multiple of 8
+  // (workgroups reach the XCDs round-robin), and its nx workgroups deal the
+  // range out in rounds of nx items.  Equal items keep the workgroups of an
+  // XCD in step, so the blocks of the few heads they work on share its L2.
+  const uint32_t npair = (uint32_t)(nqb + 1) / 2;
+  const uint32_t n_items = npair * (uint32_t)H * (uint32_t)a.batch;
   const uint32_t G = gridDim.x, g = blockIdx.x;
   const uint32_t P = G < 8 ? G : 8, pi = g % P, rank = g / P, nx = (G - pi + P - 1) / P;
   const uint32_t cnt = n_items / P + (pi < n_items % P ? 1u : 0u);
   const uint32_t beg = pi * (n_items / P) + min(pi, n_items % P);
 
   for (uint32_t rd = 0;; ++rd) {
-  const uint32_t loc = rd * nx + ((rd & 1) ? nx - 1 - rank : rank);
+  const uint32_t loc = rd * nx + rank;
   if (loc >= cnt) break;  // uniform
   const uint32_t item = beg + loc;
-  const int qb = nqb - 1 - (int)(item % (uint32_t)nqb);
-  const int h = (int)((item / (uint32_t)nqb) % (uint32_t)H), b = (int)(item / ((uint32_t)nqb * (uint32_t)H));
+  const int pr = (int)(item % npair);
+  const int h = (int)((item / npair) % (uint32_t)H), b = (int)(item / (npair * (uint32_t)H));
+  for (int half = 0; half < 2; ++half) {
+  const int qb = half == 0 ? nqb - 1 - pr : pr;  // the longer causal range first
+  if (half == 1 && qb == nqb - 1 - pr) break;    // odd nqb: the middle block once
   const int len = a.seq_lens[b];
   const int i0 = qb * kAtRows;
 
@@ -461,6 +490,7 @@ __global__ __launch_bounds__(1024) void prefill_attn_kernel(PrefillArgs a) {
       *(bf16x4*)(orow + 16 * nb) = v4;
     }
   }
+  }  // the pair's two blocks
   }  // items
 }
 
@@ -482,22 +512,24 @@ bool prefill_supports(const mla_dims_t& d, int64_t row_stride, int max_seq_len) 
   return d.q_dtype == MLA_BF16 && d.kv_dtype == MLA_BF16 && d.d_nope == 128 && d.d_v == 128 &&
          d.d_rope == 64 && d.d_latent == 512 && row_stride % 8 == 0 && row_stride <= (1 << 16) &&
          (int64_t)d.heads * 256 * 32 < ((int64_t)1 << 31) && max_seq_len <= kAtMaxPages * kTile &&
-         (int64_t)d.batch * ((max_seq_len + kExTok - 1) / kExTok) <= 65535 && d.heads <= 32767 &&
+         d.heads <= 32767 &&
          // the work-order maps index all workgroups of a launch in 32 bits
+         (int64_t)d.batch * d.heads * ((max_seq_len + kExTok - 1) / kExTok) < ((int64_t)1 << 31) &&
          (int64_t)d.batch * d.heads * ((d.q_len + kAtRows - 1) / kAtRows) < ((int64_t)1 << 31);
 }
 
 hipError_t launch_prefill_expand(const mla_dims_t& d, const PrefillArgs& a, hipStream_t s) {
   PrefillArgs x = a;
   x.ntile = (a.max_seq_len + kExTok - 1) / kExTok;
-  dim3 grid((unsigned)(2 * d.heads), (unsigned)(d.batch * x.ntile));
-  hipLaunchKernelGGL(prefill_expand_kernel, grid, dim3(256), 0, s, x);
+  const int64_t n = (int64_t)d.heads * d.batch * x.ntile;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(prefill_expand_kernel, dim3((unsigned)n), dim3(1024), 0, s, x);
   return hipGetLastError();
 }
 
 hipError_t launch_prefill_attn(const mla_dims_t& d, const PrefillArgs& a, hipStream_t s) {
   // one persistent workgroup per compute unit (fewer when there are fewer items)
-  const int64_t items = (int64_t)((d.q_len + kAtRows - 1) / kAtRows) * d.heads * d.batch;
+  const int64_t items = (int64_t)((d.q_len + kAtRows - 1) / kAtRows + 1) / 2 * d.heads * d.batch;
   const int64_t cus = cu_count();
   const unsigned grid = (unsigned)(items < cus ? items : cus);
   if (grid == 0) return hipSuccess;
