@@ -238,10 +238,10 @@ __global__ __launch_bounds__(1024) void prefill_attn_kernel(PrefillArgs a) {
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_char*)smem;
   int* prow = (int*)(smem + kAtPageOff);  // block id (paged) of each page of the item
 
-  // RoPE frequencies base^(-2p/64) of the 32 pairs, once (the first
-  // item's barrier orders them before use)
+  // RoPE frequencies base^(-2p/64) of the 32 pairs, once
   double* theta = (double*)(smem + kAtThetaOff);
   if (threadIdx.x < 32) theta[threadIdx.x] = exp2(-2.0 * (int)threadIdx.x / 64.0 * log2((double)a.rope_base));
+  block_sync();
 
   // Persistent workgroups, one per compute unit.  An item is a pair of
   // query blocks of one (sequence, head), p and nqb-1-p, whose causal
@@ -259,6 +259,7 @@ __global__ __launch_bounds__(1024) void prefill_attn_kernel(PrefillArgs a) {
   const uint32_t cnt = n_items / P + (pi < n_items % P ? 1u : 0u);
   const uint32_t beg = pi * (n_items / P) + min(pi, n_items % P);
 
+  int table_b = -1;  // sequence whose page table is in LDS
   for (uint32_t rd = 0;; ++rd) {
   const uint32_t loc = rd * nx + rank;
   if (loc >= cnt) break;  // uniform
@@ -282,13 +283,16 @@ __global__ __launch_bounds__(1024) void prefill_attn_kernel(PrefillArgs a) {
   const bool active = wrow0 < Lq;  // uniform per wave
   const int wave_vis = active ? min(len, max(0, n_vis(min(wrow0 + 15, Lq - 1)))) : 0;
 
-  // page table of the tokens this item reads; the barrier also ends the
-  // previous item's use of the ring
-  if (a.block_table) {
-    const int npg = (n_end + kTile - 1) / kTile;
+  // page table of the whole sequence, when it changes (consecutive items
+  // mostly share the sequence).  The previous block's last barrier already
+  // ended every wave's use of the ring, so with the table in place the
+  // first fills can go out at once.
+  if (a.block_table && b != table_b) {
+    const int npg = (len + kTile - 1) / kTile;
     for (int pg = (int)threadIdx.x; pg < npg; pg += 1024) prow[pg] = a.block_table[(int64_t)b * a.mbps + pg];
+    table_b = b;
+    block_sync();
   }
-  block_sync();
 
   // ---- fills: 40 blocks of 1 KB per sub-tile (keys: column groups 0-1
   // k_nope, 2 the RoPE key; values: 0-1; 8 row groups each), block k by
