@@ -24,12 +24,12 @@
 //   sequence over its keys [k_nope ; k_rope] (192 wide, the decoupled RoPE
 //   key shared by the heads) and values (128 wide).  Persistent workgroups
 //   (one per compute unit) take items of 256 query rows of one (sequence,
-//   head), 16 waves of 16 rows; the keys and values of 64 tokens (one page)
-//   at a time are filled into LDS once for all 256 rows.  Each wave computes
-//   S^T = K Q^T, the online softmax and O^T += V^T P^T on
-//   v_mfma_f32_16x16x32_bf16 with P fed from the score registers, exactly as
-//   the decode kernel does with the latent (same LDS layout and operand
-//   addressing).
+//   head), 8 waves of 32 rows; the keys and values of 64 tokens (one page)
+//   at a time are filled into LDS once for all 256 rows (the decode
+//   kernel's block layout).  Each wave computes S^T = K Q^T, the online
+//   softmax and O^T += V^T P^T on v_mfma_f32_32x32x16_bf16 with P fed from
+//   the score registers, so every key and value operand read from LDS
+//   serves 32 rows.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -215,8 +215,9 @@ __global__ __launch_bounds__(1024) void prefill_expand_kernel(PrefillArgs a) {
 
 // --------------------------------------------------------------- attention
 
-constexpr int kAtWaves = 16;
-constexpr int kAtRows = 16 * kAtWaves;          // 256 query rows per workgroup
+constexpr int kAtWaves = 8;
+constexpr int kAtRows = 32 * kAtWaves;          // 256 query rows per workgroup
+constexpr int kAtThreads = 64 * kAtWaves;
 constexpr int kAtSub = 64;                      // tokens per LDS sub-tile (one page)
 constexpr int kAtCg = kAtSub * 128;             // 8 KB: one 64-column group of the sub-tile
 constexpr int kAtKBytes = 3 * kAtCg;            // 24 KB: keys, column groups 0-2
@@ -228,7 +229,7 @@ constexpr int kAtThetaOff = kAtPageOff + kAtMaxPages * 4;
 constexpr int kAtBytes = kAtThetaOff + 32 * 8;
 static_assert(kAtBytes <= 163840, "LDS budget");
 
-__global__ __launch_bounds__(1024) void prefill_attn_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(kAtThreads) void prefill_attn_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem[kAtBytes];
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -278,10 +279,10 @@ __global__ __launch_bounds__(1024) void prefill_attn_kernel(PrefillArgs a) {
   const int n_end = min(len, max(0, n_vis(i_last)));  // tokens the workgroup reads
   const int nsub = (n_end + kAtSub - 1) / kAtSub;
 
-  // rows of this wave; lane l holds row i0 + 16w + l%16
-  const int wrow0 = i0 + 16 * w;
+  // rows of this wave; lane l holds row i0 + 32w + l%32
+  const int wrow0 = i0 + 32 * w;
   const bool active = wrow0 < Lq;  // uniform per wave
-  const int wave_vis = active ? min(len, max(0, n_vis(min(wrow0 + 15, Lq - 1)))) : 0;
+  const int wave_vis = active ? min(len, max(0, n_vis(min(wrow0 + 31, Lq - 1)))) : 0;
 
   // page table of the whole sequence, when it changes (consecutive items
   // mostly share the sequence).  The previous block's last barrier already
@@ -289,16 +290,16 @@ __global__ __launch_bounds__(1024) void prefill_attn_kernel(PrefillArgs a) {
   // first fills can go out at once.
   if (a.block_table && b != table_b) {
     const int npg = (len + kTile - 1) / kTile;
-    for (int pg = (int)threadIdx.x; pg < npg; pg += 1024) prow[pg] = a.block_table[(int64_t)b * a.mbps + pg];
+    for (int pg = (int)threadIdx.x; pg < npg; pg += kAtThreads) prow[pg] = a.block_table[(int64_t)b * a.mbps + pg];
     table_b = b;
     block_sync();
   }
 
   // ---- fills: 40 blocks of 1 KB per sub-tile (keys: column groups 0-1
-  // k_nope, 2 the RoPE key; values: 0-1; 8 row groups each), block k by
-  // wave k % 16; all of a wave's blocks are row group w & 7
-  const int n_share = w < 8 ? 3 : 2;
-  const int rg = w & 7;
+  // k_nope, 2 the RoPE key; values: 0-1; 8 row groups each); wave w issues
+  // blocks w + 8i, all of row group w
+  constexpr int n_share = 5;
+  const int rg = w;
   int pz = 0;  // next sub-tile to fill
   auto issue = [&]() {
     // lane offsets from an opaque lane id: recomputed here, not kept live
@@ -310,9 +311,8 @@ __global__ __launch_bounds__(1024) void prefill_attn_kernel(PrefillArgs a) {
     const uint32_t slot = lds0 + (uint32_t)((pz % kAtRing) * kAtSubBytes);
     const int tl = min(t0 + 8 * rg + rho, len - 1) - t0;  // clamped rows are masked
 #pragma unroll
-    for (int i = 0; i < 3; ++i) {
-      const int k = w + 16 * i;
-      if (k >= 40) break;  // uniform
+    for (int i = 0; i < n_share; ++i) {
+      const int k = w + 8 * i;
       if (k < 16 || k >= 24) {  // k_nope or v: [B, Tmax, H, 128]
         const int cg = (k < 16 ? k : k - 24) >> 3;
         const char* base = (const char*)(k < 16 ? a.k_nope : a.v) + (((int64_t)b * Tmax + t0) * H + h) * 256;
@@ -334,28 +334,30 @@ __global__ __launch_bounds__(1024) void prefill_attn_kernel(PrefillArgs a) {
   // overlap
   for (int z = 0; z < kAtRing - 1 && z < nsub; ++z) issue();
 
-  // ---- the wave's query rows: q_nope in k-slices 0-3, RoPE(q_rope) in 4-5
-  bf16x8 q[6];
+  // ---- the wave's query rows as the B operand of the score products: lane
+  // l holds row l%32 and, for k-step k (16 dims), dims 16k + 8(l/32)..+7:
+  // q_nope for k < 8, RoPE(q_rope) for k = 8..11
+  bf16x8 q[12];
   {
     const int fl = fresh_lane();
-    const int li = fl & 15, gq = fl >> 4;
+    const int li = fl & 31, hq = fl >> 5;
     const int i = min(wrow0 + li, Lq - 1);
     const int64_t qrow = ((int64_t)b * Lq + i) * H + h;
     const bf16x8* qn = (const bf16x8*)((const uint16_t*)a.q_nope + qrow * 128);
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) q[kk] = qn[4 * kk + gq];
+    for (int k = 0; k < 8; ++k) q[k] = qn[2 * k + hq];
     const bf16x8* qr = (const bf16x8*)((const uint16_t*)a.q_rope + qrow * 64);
     const double pos = (double)a.positions[(int64_t)b * Lq + i];
 #pragma unroll
-    for (int kk = 4; kk < 6; ++kk) {
-      const bf16x8 x = qr[4 * (kk - 4) + gq];
+    for (int k = 8; k < 12; ++k) {
+      const int un = 2 * (k - 8) + hq;  // 8-dim unit of q_rope
+      const bf16x8 x = qr[un];
       bf16x8 y;
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        // pair p = 16 (kk-4) + 4 gq + m turns by pos * base^(-2p/64); the
-        // angle is reduced modulo 2 pi in double, sin/cos in single
-        const int pr = 16 * (kk - 4) + 4 * gq + m;
-        double ang = pos * theta[pr];
+        // pair p = 4 un + m turns by pos * base^(-2p/64); the angle is
+        // reduced modulo 2 pi in double, sin/cos in single
+        double ang = pos * theta[4 * un + m];
         ang -= 6.283185307179586 * rint(ang * 0.15915494309189535);
         float sn, cs;
         __sincosf((float)ang, &sn, &cs);
@@ -363,19 +365,19 @@ __global__ __launch_bounds__(1024) void prefill_attn_kernel(PrefillArgs a) {
         y[2 * m] = (__bf16)(x0 * cs - x1 * sn);
         y[2 * m + 1] = (__bf16)(x0 * sn + x1 * cs);
       }
-      q[kk] = y;
+      q[k] = y;
     }
     // taken here: the compiler's waits for the query (it does not count
     // the direct loads issued before them) then also cover sub-tiles 0-1
 #pragma unroll
-    for (int kk = 0; kk < 6; ++kk) asm volatile("" ::"v"(q[kk]));
+    for (int k = 0; k < 12; ++k) asm volatile("" ::"v"(q[k]));
   }
   if (nsub > 0) wait_vm(n_share * (pz - 1));
   block_sync();
 
-  f32x4 o[8];  // O^T: block nb holds value columns 16 nb + 4(l/16)..+3 of row l%16
+  f32x16 o[4];  // O^T tile ct: value columns 32 ct + 8(r/4) + 4(l/32) + r%4 of row l%32
 #pragma unroll
-  for (int nb = 0; nb < 8; ++nb) o[nb] = f32x4{};
+  for (int ct = 0; ct < 4; ++ct) o[ct] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
   const float sl2 = a.softmax_scale * kLog2e;
 
@@ -384,87 +386,104 @@ __global__ __launch_bounds__(1024) void prefill_attn_kernel(PrefillArgs a) {
     const char* tile = smem + (s % kAtRing) * kAtSubBytes;
     const int t0 = s * kAtSub;
     if (active && t0 < wave_vis) {  // uniform per wave
-      f32x4 sc[4];  // token block jt: tokens 16 jt + 4(l/16)..+3
-#pragma unroll
-      for (int jt = 0; jt < 4; ++jt) sc[jt] = f32x4{};
+      // ---- S^T = K Q^T on v_mfma_f32_32x32x16_bf16, two 32-token tiles jt:
+      // lane l ends with row l%32 and tokens 32 jt + 8(r/4) + 4(l/32) + r%4
+      f32x16 sc[2] = {f32x16{}, f32x16{}};
       {
+        const int lk = fresh_lane();
+        const int tk = lk & 31, hk = lk >> 5, rgk = tk >> 3, rhk = tk & 7;
+        // K operand of k-step k, tile jt: token 32 jt + tk, dims 16k + 8hk..+7,
+        // at kb[k % 4] + (k / 4) * 8 KB + jt * 4 KB
+        uint32_t kb[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int kap = 2 * j + hk;
+          kb[j] = (uint32_t)(rgk * 1024 + 16 * (8 * (kap ^ (rgk & 1)) + (rhk ^ (4 * ((kap ^ (kap >> 1)) & 1)))));
+        }
+        auto kaddr = [&](int k, int jt) { return kb[k & 3] + (uint32_t)((k >> 2) * kAtCg + jt * 4096); };
         constexpr int kPf = 2;
-        const uint32_t o_qk = off_qk(fresh_lane());
-        bf16x8 ka[kPf + 1][4];
-        auto kload = [&](int kk) {
-          const int e = kk % (kPf + 1);
+        bf16x8 ka[kPf + 1][2];
 #pragma unroll
-          for (int jt = 0; jt < 4; ++jt)
-            ka[e][jt] = *(const bf16x8*)(tile + (uint32_t)((kk >> 1) * kAtCg + 2048 * jt + 512 * (kk & 1)) + o_qk);
-        };
+        for (int k = 0; k < kPf; ++k)
 #pragma unroll
-        for (int kk = 0; kk < kPf; ++kk) kload(kk);
+          for (int jt = 0; jt < 2; ++jt) ka[k][jt] = *(const bf16x8*)(tile + kaddr(k, jt));
 #pragma unroll
-        for (int kk = 0; kk < 6; ++kk) {
-          if (kk + kPf < 6) kload(kk + kPf);
-          const int e = kk % (kPf + 1);
+        for (int k = 0; k < 12; ++k) {
+          if (k + kPf < 12)
 #pragma unroll
-          for (int jt = 0; jt < 4; ++jt) sc[jt] = mfma16(ka[e][jt], q[kk], sc[jt]);
+            for (int jt = 0; jt < 2; ++jt) ka[(k + kPf) % (kPf + 1)][jt] = *(const bf16x8*)(tile + kaddr(k + kPf, jt));
+#pragma unroll
+          for (int jt = 0; jt < 2; ++jt) sc[jt] = mfma32(ka[k % (kPf + 1)][jt], q[k], sc[jt]);
           __builtin_amdgcn_sched_barrier(0);
         }
-#pragma unroll
-        for (int jt = 0; jt < 4; ++jt) mfma_settle(sc[jt]);
       }
       const int ln = fresh_lane();
-      const int nv = min(len, n_vis(wrow0 + (ln & 15)));  // this lane's row
+      const int hk = ln >> 5;
+      const int nv = min(len, n_vis(wrow0 + (ln & 31)));  // this lane's row
       if (t0 + kAtSub > nv) {  // mask past the visible end
 #pragma unroll
-        for (int jt = 0; jt < 4; ++jt)
+        for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (t0 + 16 * jt + 4 * (ln >> 4) + r >= nv) sc[jt][r] = -INFINITY;
+          for (int r = 0; r < 16; ++r)
+            if (t0 + 32 * jt + 8 * (r >> 2) + 4 * hk + (r & 3) >= nv) sc[jt][r] = -INFINITY;
       }
       // lazy rescale: the reference max moves only when a score passes it
-      // by more than 2^8 (log2 units)
+      // by more than 2^8 (log2 units); a row's scores sit in lanes l, l^32
       float lm = sc[0][0];
 #pragma unroll
-      for (int jt = 0; jt < 4; ++jt)
+      for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) lm = fmaxf(lm, sc[jt][r]);
+        for (int r = 0; r < 16; ++r) lm = fmaxf(lm, sc[jt][r]);
       lm *= sl2;
       if (__ballot(lm > m_run + 8.f) != 0) {
-        float mt = fmaxf(lm, __shfl_xor(lm, 16, 64));
-        mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+        const float mt = fmaxf(lm, __shfl_xor(lm, 32, 64));
         const float m_new = fmaxf(m_run, mt);
         const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
         m_run = m_new;
         l_run *= alpha;
 #pragma unroll
-        for (int nb = 0; nb < 8; ++nb) o[nb] *= alpha;
+        for (int ct = 0; ct < 4; ++ct) o[ct] *= alpha;
       }
       const float m_use = m_run == -INFINITY ? 0.f : m_run;
-      // P^T operands of the two 32-token halves ks: tokens
-      // {32 ks + 4(l/16)..+3, 32 ks + 16 + 4(l/16)..+3} of row l%16
-      bf16x8 p[2];
+      // P^T operand of value k-step ks (16 tokens): registers 8(ks%2)..+7 of
+      // tile ks/2, i.e. tokens 16 ks + 4(l/32) + {0..3, 8..11}
+      bf16x8 p[4];
 #pragma unroll
-      for (int jt = 0; jt < 4; ++jt)
+      for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
+        for (int r = 0; r < 16; ++r) {
           const float e = __builtin_amdgcn_exp2f(fmaf(sc[jt][r], sl2, -m_use));
           l_run += e;
-          p[jt >> 1][4 * (jt & 1) + r] = (__bf16)e;
+          p[2 * jt + (r >> 3)][r & 7] = (__bf16)e;
         }
-      // O^T += V^T P^T, V^T read transposed from the values' blocks (the
-      // second half's row groups sit 4 KB after the first's)
+      // ---- O^T += V^T P^T: V^T (32 columns x 16 tokens) read transposed.
+      // Lane l (G = l/16, i = l%16) names token 16 ks + 8 sub + 4(G/2) + i/4
+      // and columns 32 ct + 16(G&1) + 4(i%4)..+3, and then holds column
+      // 32 ct + l%32 and 4 consecutive tokens; the address is
+      // vb[ct % 2][sub] + (ct / 2) * 8 KB + ks * 2 KB.
       const char* vt = tile + kAtKBytes;
       const int lv = fresh_lane();
-      const uint32_t vb00 = vt_base(lv, 0, 0), vb01 = vt_base(lv, 0, 1);
-      const uint32_t vb10 = vt_base(lv, 1, 0), vb11 = vt_base(lv, 1, 1);
-      auto vload = [&](int n) {  // n = 2 nb + ks
-        const int nb = n >> 1, ks = n & 1;
-        const uint32_t cb = (uint32_t)((nb >> 2) * kAtCg + ks * 4096 + (nb & 3) * 256);
-        return cat(lds_tr4(vt, cb + ((nb & 1) ? vb01 : vb00)), lds_tr4(vt, cb + ((nb & 1) ? vb11 : vb10)));
+      const int G = lv >> 4, i16 = lv & 15;
+      uint32_t vb[2][2];
+#pragma unroll
+      for (int par = 0; par < 2; ++par)
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub) {
+          const int kap = 4 * par + 2 * (G & 1) + ((i16 & 3) >> 1);
+          const int rho = 4 * (G >> 1) + (i16 >> 2);
+          vb[par][sub] = (uint32_t)(sub * 1024 + 16 * (8 * (kap ^ sub) + (rho ^ (4 * ((kap ^ (kap >> 1)) & 1)))) +
+                                    8 * (i16 & 1));
+        }
+      auto vload = [&](int n) {  // n = 4 ks + ct
+        const int ks = n >> 2, ct = n & 3;
+        const uint32_t off = (uint32_t)((ct >> 1) * kAtCg + ks * 2048);
+        return cat(lds_tr4(vt, vb[ct & 1][0] + off), lds_tr4(vt, vb[ct & 1][1] + off));
       };
       bf16x8 va = vload(0), vn = vload(1);
 #pragma unroll
       for (int n = 0; n < 16; ++n) {
         const bf16x8 vnn = n + 2 < 16 ? vload(n + 2) : vn;
-        o[n >> 1] = mfma16(va, p[n & 1], o[n >> 1]);
+        o[n & 3] = mfma32(va, p[n >> 2], o[n & 3]);
         __builtin_amdgcn_sched_barrier(0);
         va = vn;
         vn = vnn;
@@ -475,24 +494,25 @@ __global__ __launch_bounds__(1024) void prefill_attn_kernel(PrefillArgs a) {
     block_sync();  // sub-tile s+1 complete for everyone; the slot of s free
   }
 #pragma unroll
-  for (int nb = 0; nb < 8; ++nb) mfma_settle(o[nb]);
+  for (int ct = 0; ct < 4; ++ct) mfma_settle(o[ct]);
 
   // ---- outputs: o = O / l (0 where no token was visible), lse
-  float l_tot = l_run + __shfl_xor(l_run, 16, 64);
-  l_tot += __shfl_xor(l_tot, 32, 64);
+  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   const int lw = fresh_lane();
-  const int i = wrow0 + (lw & 15);
+  const int i = wrow0 + (lw & 31);
   if (active && i < Lq) {
     const int64_t row = ((int64_t)b * Lq + i) * H + h;
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    if (a.lse && (lw >> 4) == 0) a.lse[row] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
-    uint16_t* orow = (uint16_t*)a.o + row * 128 + 4 * (lw >> 4);
+    if (a.lse && (lw >> 5) == 0) a.lse[row] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+    uint16_t* orow = (uint16_t*)a.o + row * 128 + 4 * (lw >> 5);
 #pragma unroll
-    for (int nb = 0; nb < 8; ++nb) {
-      const bf16x4 v4 = {(__bf16)(o[nb][0] * inv), (__bf16)(o[nb][1] * inv), (__bf16)(o[nb][2] * inv),
-                         (__bf16)(o[nb][3] * inv)};
-      *(bf16x4*)(orow + 16 * nb) = v4;
-    }
+    for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const bf16x4 v4 = {(__bf16)(o[ct][4 * g] * inv), (__bf16)(o[ct][4 * g + 1] * inv),
+                           (__bf16)(o[ct][4 * g + 2] * inv), (__bf16)(o[ct][4 * g + 3] * inv)};
+        *(bf16x4*)(orow + 32 * ct + 8 * g) = v4;
+      }
   }
   }  // the pair's two blocks
   }  // items
@@ -537,7 +557,7 @@ hipError_t launch_prefill_attn(const mla_dims_t& d, const PrefillArgs& a, hipStr
   const int64_t cus = cu_count();
   const unsigned grid = (unsigned)(items < cus ? items : cus);
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL(prefill_attn_kernel, dim3(grid), dim3(1024), 0, s, a);
+  hipLaunchKernelGGL(prefill_attn_kernel, dim3(grid), dim3(kAtThreads), 0, s, a);
   return hipGetLastError();
 }
 
