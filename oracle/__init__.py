@@ -9,11 +9,13 @@ from .mla_oracle import (
     bf16_to_f64,
     cache_f64,
     e4m3_to_f64,
+    fuse_out_weight,
     kv_append,
     kv_cache_bytes_per_token,
     mla_absorbed,
     mla_decode,
     mla_expand,
+    out_proj_fused,
     rms_norm,
     rope_interleaved,
     stored_to_f64,
@@ -23,11 +25,13 @@ __all__ = [
     "bf16_to_f64",
     "cache_f64",
     "e4m3_to_f64",
+    "fuse_out_weight",
     "kv_append",
     "kv_cache_bytes_per_token",
     "mla_absorbed",
     "mla_decode",
     "mla_expand",
+    "out_proj_fused",
     "rms_norm",
     "rope_interleaved",
     "stored_to_f64",

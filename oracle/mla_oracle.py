@@ -32,6 +32,9 @@ Readings where the pages leave a step open:
   * The cache-append producer (``kv_append``): RMSNorm with eps as given by
     the caller (the module on [MATH] uses the framework default); the new
     token's key is rotated at its own position.
+  * Output-side absorption (``fuse_out_weight``, ``out_proj_fused``): W_O is
+    d x (H d_v) with head i's block in columns i d_v .. (i+1) d_v; the fused
+    weight is kept as [d, H, d_c].
 """
 
 from __future__ import annotations
@@ -293,6 +296,40 @@ def kv_append(h, w_dkv, kv_norm_w, w_kr, pos, rope_base: float, eps: float):
     c_kv = rms_norm(c, kv_norm_w, eps)
     k_rope = rope_interleaved(h @ np.asarray(w_kr, np.float64).T, np.asarray(pos), rope_base)
     return c_kv, k_rope
+
+
+# ------------------------------------------- output-side absorption
+
+
+def fuse_out_weight(w_o, w_uv, heads: int):
+    """The pre-fused output weight of each head ([ARCH] 3.2: W~_O,i =
+    W_O,i W_UV,i in R^{d x d_c}; [MATH] value output matrix absorption:
+    W_O = [W_O^1, ..., W_O^{n_h}] in R^{d x (n_h d_v)}).
+
+    w_o: [d, H * d_v] (column block i is W_O,i); w_uv: [H, d_v, d_c].
+    Returns [d, H, d_c] float64 (the layout of a map from the H x d_c latent
+    outputs to the d-wide hidden state).
+    """
+    w_o = np.asarray(w_o, np.float64)
+    w_uv = np.asarray(w_uv, np.float64)
+    d = w_o.shape[0]
+    d_v = w_uv.shape[1]
+    out = np.empty((d, heads, w_uv.shape[2]))
+    for i in range(heads):
+        out[:, i, :] = w_o[:, i * d_v:(i + 1) * d_v] @ w_uv[i]
+    return out
+
+
+def out_proj_fused(o_lat, w_fused):
+    """The hidden-state contribution of the attention block straight from the
+    latent outputs ([ARCH] 3.2: u_t = sum_i W~_O,i o~_{t,i}).
+
+    o_lat: [M, H, d_c] (one row per query token); w_fused: [d, H, d_c].
+    Returns [M, d] float64.
+    """
+    o = np.asarray(o_lat, np.float64)
+    w = np.asarray(w_fused, np.float64)
+    return o.reshape(o.shape[0], -1) @ w.reshape(w.shape[0], -1).T
 
 
 # ------------------------------------------------------- byte accounting

@@ -17,8 +17,8 @@ import torch
 
 from mla_inputs import CONFIGS, MLAInputs, scaled
 from mla_inputs.generate import bf16_bits_from_f32
-from oracle import (bf16_to_f64, e4m3_to_f64, kv_cache_bytes_per_token, mla_absorbed,
-                    mla_decode, mla_expand, rope_interleaved)
+from oracle import (bf16_to_f64, e4m3_to_f64, fuse_out_weight, kv_cache_bytes_per_token,
+                    mla_absorbed, mla_decode, mla_expand, out_proj_fused, rope_interleaved)
 from tests._fake import ArrayInputs, random_arrays
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -434,3 +434,63 @@ def test_kv_append_norm_invariants():
     np.testing.assert_allclose(ckv3, ckv, rtol=1e-13, atol=1e-15)
     np.testing.assert_allclose(kr, h @ wr.T, rtol=1e-13, atol=1e-15)
     np.testing.assert_allclose(kr3, 3.0 * kr, rtol=1e-13, atol=1e-15)
+
+
+# ------------------------------------------------- output-side absorption
+
+
+def test_fused_output_weight_equals_unfused_projection():
+    """u[m] = sum_i W~_O,i o_lat[m, i] with the pre-fused weight equals the
+    unfused definition, per-head values v_i = W_UV,i o_lat[m, i] and then W_O
+    over their concatenation, written out with scalar loops."""
+    rng = np.random.default_rng(41)
+    H, d_v, d_c, d, M = 3, 4, 5, 7, 2
+    w_o = rng.standard_normal((d, H * d_v))
+    w_uv = rng.standard_normal((H, d_v, d_c))
+    o_lat = rng.standard_normal((M, H, d_c))
+    got = out_proj_fused(o_lat, fuse_out_weight(w_o, w_uv, H))
+    assert got.shape == (M, d)
+    for m in range(M):
+        concat = []
+        for i in range(H):
+            for j in range(d_v):
+                concat.append(sum(w_uv[i, j, c] * o_lat[m, i, c] for c in range(d_c)))
+        for n in range(d):
+            ref = sum(w_o[n, k] * concat[k] for k in range(H * d_v))
+            assert abs(got[m, n] - ref) < 1e-12
+
+
+def test_fused_output_weight_with_identity_w_o():
+    """With W_O the identity (d = H d_v) the fused weight of head i is W_UV,i
+    placed in rows i d_v .. (i+1) d_v, and the fused projection returns the
+    concatenated per-head values."""
+    rng = np.random.default_rng(42)
+    H, d_v, d_c = 4, 3, 6
+    w_uv = rng.standard_normal((H, d_v, d_c))
+    wf = fuse_out_weight(np.eye(H * d_v), w_uv, H)
+    for i in range(H):
+        np.testing.assert_array_equal(wf[i * d_v:(i + 1) * d_v, i, :], w_uv[i])
+        others = [k for k in range(H * d_v) if not (i * d_v <= k < (i + 1) * d_v)]
+        assert np.all(wf[others, i, :] == 0.0)
+    o_lat = rng.standard_normal((5, H, d_c))
+    got = out_proj_fused(o_lat, wf)
+    ref = np.concatenate([o_lat[:, i, :] @ w_uv[i].T for i in range(H)], axis=1)
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
+
+
+def test_fused_output_projection_of_the_attention_output():
+    """Applied to the absorbed latent output of the attention, the fused path
+    gives W_O times the concatenated non-absorbed head outputs (the oracle's
+    decode output, pinned separately)."""
+    arr = _arrays(43, B=2, Lq=2, lens=(6, 4))
+    inp = ArrayInputs(**arr, causal=True)
+    d = DIMS
+    o = mla_decode(inp)["o"]             # [B, Lq, H, d_v]
+    o_lat = mla_absorbed(inp)["o_lat"]   # [B, Lq, H, d_c]
+    rng = np.random.default_rng(44)
+    d_model = 9
+    w_o = rng.standard_normal((d_model, d["H"] * d["d_v"]))
+    wf = fuse_out_weight(w_o, inp.w_uv, d["H"])
+    got = out_proj_fused(o_lat.reshape(-1, d["H"], d["d_c"]), wf)
+    ref = o.reshape(-1, d["H"] * d["d_v"]) @ w_o.T
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-10)
