@@ -366,6 +366,51 @@ int mla_prefill_attn(const mla_dims_t* dims, const void* q_nope, const void* q_r
                      int32_t max_blocks_per_seq, int32_t block_size, int32_t max_seq_len,
                      int32_t causal, float softmax_scale, void* o, float* lse, void* stream);
 
+/*
+ * ---- Output-side absorption ([ARCH] 3.2 and 4.2; [MATH] "Value Output
+ * Matrix Absorption").  The value up-projection W_UV,i of head i and that
+ * head's d x d_v block W_O,i of the output projection W_O = [W_O,1 ... W_O,H]
+ * act back to back on the latent output, so they can be multiplied once,
+ * when the model is loaded, into W~_O,i = W_O,i W_UV,i (d x d_c); the
+ * attention's latent outputs then map straight to the hidden width,
+ *   u = sum_i W~_O,i o~_i.
+ * Built for q_dtype MLA_BF16, d_latent 512, d_v <= 128, heads <= 1024,
+ * d_model <= 65536 and batch * q_len * d_model < 2^31; anything else
+ * returns MLA_ERR_UNSUPPORTED.  kv_dtype is not used.
+ */
+
+/*
+ * mla_fuse_out_weight -- the fused weight, once per layer (load time).
+ *
+ *   w_o      [d_model, H * d_v]   bf16, columns i*d_v .. i*d_v+d_v-1 are W_O,i
+ *   w_uv     [H, d_v, d_latent]   bf16 (as in mla_out_proj)
+ *   w_fused  [d_model, H, d_latent] bf16, output:
+ *            w_fused[n, i, c] = sum_j w_o[n, i*d_v + j] * w_uv[i, j, c]
+ *            (fp32 accumulate, one rounding to bf16)
+ */
+int mla_fuse_out_weight(const mla_dims_t* dims, int32_t d_model, const void* w_o,
+                        const void* w_uv, void* w_fused, void* stream);
+
+/* Bytes of the fp32 workspace mla_out_proj_fused needs: 8 * batch * q_len
+ * * d_model * 4 (partial sums of eight slices of the H * d_latent inputs). */
+int mla_out_proj_fused_workspace_bytes(const mla_dims_t* dims, int32_t d_model, int64_t* bytes);
+
+/*
+ * mla_out_proj_fused -- the block output from the latent attention output.
+ *
+ *   o_lat     [B, Lq, H, d_latent] bf16 (mla_combine's o_lat)
+ *   w_fused   [d_model, H, d_latent] bf16 (mla_fuse_out_weight's output)
+ *   workspace mla_out_proj_fused_workspace_bytes() bytes, 16-byte aligned;
+ *             overwritten (no initial contents needed)
+ *   out       [B, Lq, d_model] bf16, output:
+ *             out[b, t, n] = sum_{i, c} w_fused[n, i, c] * o_lat[b, t, i, c]
+ *             (fp32 accumulate; the eight slice sums are added in a fixed
+ *             order, so results repeat bit for bit)
+ * batch == 0 returns MLA_OK with nothing enqueued.
+ */
+int mla_out_proj_fused(const mla_dims_t* dims, int32_t d_model, const void* o_lat,
+                       const void* w_fused, void* workspace, void* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

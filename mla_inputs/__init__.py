@@ -8,7 +8,7 @@ oracle and the GPU path consume what it produces.
 """
 
 from .configs import BLOCK_TOKENS, CONFIGS, HEADLINE, PREFILL_CONFIGS, MLAConfig, scaled
-from .generate import AppendInputs, MLAInputs, Pool
+from .generate import AppendInputs, MLAInputs, OutProjInputs, Pool
 
 __all__ = [
     "AppendInputs",
@@ -17,6 +17,7 @@ __all__ = [
     "HEADLINE",
     "MLAConfig",
     "MLAInputs",
+    "OutProjInputs",
     "PREFILL_CONFIGS",
     "Pool",
     "scaled",

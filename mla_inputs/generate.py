@@ -242,3 +242,34 @@ class AppendInputs:
         pool = self.pool_rows or 2 * n + 1
         self.pool_rows = pool
         self.rows = _rng(self.seed, _T_APP_ROWS).permutation(pool)[:n].astype(np.int64)
+
+
+# Tensor ids of the output-side absorption's streams.
+_T_OUT_OLAT, _T_OUT_WO, _T_OUT_WUV = range(201, 204)
+
+
+@dataclass
+class OutProjInputs:
+    """Seeded inputs of the output-side absorption (bf16 bit patterns).
+
+    o_lat ~ N(0, 1) [m, heads, d_latent] (the attention's latent outputs of
+    m query tokens); w_o ~ N(0, 1/(heads d_v)) [d_model, heads d_v];
+    w_uv ~ N(0, 1/d_latent) [heads, d_v, d_latent].
+    """
+    m: int
+    heads: int
+    d_model: int
+    seed: int
+    d_v: int = 128
+    d_latent: int = 512
+
+    def __post_init__(self):
+        f32 = np.float32
+        H, dv, dc = self.heads, self.d_v, self.d_latent
+        self.o_lat = bf16_bits_from_f32(
+            _rng(self.seed, _T_OUT_OLAT).standard_normal((self.m, H, dc), dtype=f32))
+        self.w_o = bf16_bits_from_f32(
+            _rng(self.seed, _T_OUT_WO).standard_normal((self.d_model, H * dv), dtype=f32)
+            / f32(np.sqrt(H * dv)))
+        self.w_uv = bf16_bits_from_f32(
+            _rng(self.seed, _T_OUT_WUV).standard_normal((H, dv, dc), dtype=f32) / f32(np.sqrt(dc)))

@@ -73,6 +73,9 @@ def _load():
         "mla_prefill_expand": [P, VP, I64, VP, VP, I32, I32, I32, VP, VP, VP, VP, VP],
         "mla_prefill_attn": [P, VP, VP, VP, F, VP, VP, VP, I64, VP, VP, I32, I32, I32, I32, F, VP,
                              VP, VP],
+        "mla_fuse_out_weight": [P, I32, VP, VP, VP, VP],
+        "mla_out_proj_fused_workspace_bytes": [P, I32, ctypes.POINTER(I64)],
+        "mla_out_proj_fused": [P, I32, VP, VP, VP, VP, VP],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -240,3 +243,22 @@ def mla_prefill_attn(d: MLADims, q_nope, q_rope, positions, rope_base, k_nope, v
                                  int(causal), float(softmax_scale), _ptr(o), _ptr(lse),
                                  _stream(stream)),
            "mla_prefill_attn")
+
+
+def mla_fuse_out_weight(d: MLADims, d_model, w_o, w_uv, w_fused, stream=None):
+    _check(_lib.mla_fuse_out_weight(ctypes.byref(d), int(d_model), _ptr(w_o), _ptr(w_uv),
+                                    _ptr(w_fused), _stream(stream)),
+           "mla_fuse_out_weight")
+
+
+def mla_out_proj_fused_workspace_bytes(d: MLADims, d_model) -> int:
+    out = ctypes.c_int64()
+    _check(_lib.mla_out_proj_fused_workspace_bytes(ctypes.byref(d), int(d_model), ctypes.byref(out)),
+           "mla_out_proj_fused_workspace_bytes")
+    return out.value
+
+
+def mla_out_proj_fused(d: MLADims, d_model, o_lat, w_fused, workspace, out, stream=None):
+    _check(_lib.mla_out_proj_fused(ctypes.byref(d), int(d_model), _ptr(o_lat), _ptr(w_fused),
+                                   _ptr(workspace), _ptr(out), _stream(stream)),
+           "mla_out_proj_fused")

@@ -21,7 +21,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmla.so")
 SOURCES = ["mla_api.hip", "generic_kernels.hip", "combine.hip", "mfma_kernels.hip", "decode_split.hip",
-           "combine_proj.hip", "kv_append.hip", "prefill.hip"]
+           "combine_proj.hip", "kv_append.hip", "prefill.hip", "out_fused.hip"]
 ARCH = "gfx950"
 
 

@@ -81,4 +81,12 @@ hipError_t launch_combine_proj(const mla_dims_t& d, int num_splits, const int32_
 hipError_t launch_out_proj_mfma(const mla_dims_t& d, const void* o_lat, const void* w_uv,
                                 void* o, hipStream_t s);
 
+// Output-side absorption (bf16, latent 512, d_v <= 128).
+bool out_fused_supports(const mla_dims_t& d, int d_model);
+hipError_t launch_fuse_out(const mla_dims_t& d, int d_model, const void* w_o, const void* w_uv,
+                           void* w_fused, hipStream_t s);
+int64_t out_fused_workspace_floats(const mla_dims_t& d, int d_model);
+hipError_t launch_out_fused(const mla_dims_t& d, int d_model, const void* o_lat, const void* w_fused,
+                            float* workspace, void* out, hipStream_t s);
+
 }  // namespace mla

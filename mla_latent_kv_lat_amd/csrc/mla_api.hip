@@ -335,4 +335,42 @@ int mla_prefill_attn(const mla_dims_t* dims, const void* q_nope, const void* q_r
   return launched(launch_prefill_attn(*dims, a, (hipStream_t)stream));
 }
 
+// ---- Output-side absorption ----
+
+int mla_fuse_out_weight(const mla_dims_t* dims, int32_t d_model, const void* w_o, const void* w_uv,
+                        void* w_fused, void* stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (d_model < 1 || !w_o || !w_uv || !w_fused) return MLA_ERR_INVALID_ARG;
+  if (!aligned16(w_o) || !aligned16(w_uv) || !aligned16(w_fused)) return MLA_ERR_INVALID_ARG;
+  if (!out_fused_supports(*dims, d_model)) return MLA_ERR_UNSUPPORTED;
+  (void)hipGetLastError();
+  return launched(launch_fuse_out(*dims, d_model, w_o, w_uv, w_fused, (hipStream_t)stream));
+}
+
+int mla_out_proj_fused_workspace_bytes(const mla_dims_t* dims, int32_t d_model, int64_t* bytes) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (d_model < 1 || !bytes) return MLA_ERR_INVALID_ARG;
+  if (!out_fused_supports(*dims, d_model)) return MLA_ERR_UNSUPPORTED;
+  *bytes = out_fused_workspace_floats(*dims, d_model) * 4;
+  return MLA_OK;
+}
+
+int mla_out_proj_fused(const mla_dims_t* dims, int32_t d_model, const void* o_lat,
+                       const void* w_fused, void* workspace, void* out, void* stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (d_model < 1) return MLA_ERR_INVALID_ARG;
+  if (!out_fused_supports(*dims, d_model)) return MLA_ERR_UNSUPPORTED;
+  if (dims->batch == 0) return MLA_OK;
+  if (!o_lat || !w_fused || !out) return MLA_ERR_INVALID_ARG;
+  if (!workspace) return MLA_ERR_WORKSPACE;
+  if (!aligned16(o_lat) || !aligned16(w_fused) || !aligned16(workspace) || !aligned16(out))
+    return MLA_ERR_INVALID_ARG;
+  (void)hipGetLastError();
+  return launched(launch_out_fused(*dims, d_model, o_lat, w_fused, (float*)workspace, out,
+                                   (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -255,3 +255,34 @@ def test_prefill_validation():
     assert attn(d, rope_base=float("inf")) == 1
     assert expand(d, w_uv=None) == 1
     assert attn(_d(q_len=256, q_dtype=mla.F32, kv_dtype=mla.F32)) == 2
+
+
+def test_out_fused_validation():
+    """Output-side absorption calls: host checks before anything is enqueued
+    (every pointer here is a fake, so any launch would fault)."""
+    lib = binding.library()
+    d = _d(batch=64)
+
+    def fuse(dd, d_model=7168, w_o=16, w_uv=16, w_fused=16):
+        return lib.mla_fuse_out_weight(ctypes.byref(dd), d_model, w_o, w_uv, w_fused, None)
+
+    def proj(dd, d_model=7168, o_lat=16, w_fused=16, workspace=16, out=16):
+        return lib.mla_out_proj_fused(ctypes.byref(dd), d_model, o_lat, w_fused, workspace, out, None)
+
+    assert fuse(d, w_o=None) == 1
+    assert fuse(d, w_fused=8) == 1                               # misaligned
+    assert fuse(d, d_model=0) == 1
+    assert fuse(_d(d_latent=256)) == 2
+    assert fuse(_d(d_v=256)) == 2
+    assert fuse(_d(q_dtype=mla.F32, kv_dtype=mla.F32)) == 2
+    assert fuse(d, d_model=65537) == 2
+    assert proj(_d(batch=0)) == 0                                # nothing to do
+    assert proj(d, workspace=None) == 3
+    assert proj(d, out=None) == 1
+    assert proj(d, o_lat=24) == 1
+    assert proj(_d(d_latent=256)) == 2
+    assert proj(_d(batch=1 << 20)) == 2                          # rows x d_model past 2^31
+    n = ctypes.c_int64()
+    assert lib.mla_out_proj_fused_workspace_bytes(ctypes.byref(d), 7168, ctypes.byref(n)) == 0
+    assert n.value == 8 * 64 * 7168 * 4
+    assert mla.mla_out_proj_fused_workspace_bytes(_d(batch=3, q_len=2), 100) == 8 * 6 * 100 * 4
