@@ -4,7 +4,10 @@
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 
 `--workload prefill_b4_s4k` measures the MHA-form prefill instead (a step
-is mla_prefill_expand + mla_prefill_attn; value in TFLOP/s).
+is mla_prefill_expand + mla_prefill_attn; value in TFLOP/s), and
+`--workload out_fused_dsv3_m64` (or `_m128`) the output-side absorption
+(a step is one mla_out_proj_fused call through the pre-fused W_O W_UV;
+value in GB/s of the fused weight stream).
 
 A step is the whole hot path on one batch of synthetic inputs already
 resident in GPU memory: mla_absorb_q (W_UK absorption + query RoPE),
@@ -334,6 +337,149 @@ def prefill_cpu_baseline(inp, acc, seconds: float):
                       "conversion of its inputs); value = the sample's share of the prefill flops / time"}
 
 
+def out_fused_main(args, name, torch):
+    """The projection of one decode step's latent outputs through the
+    pre-fused output weight (mla_out_proj_fused); a step is one call.  The
+    unfused alternative's W_O product (a plain library GEMM on the W_UV
+    outputs) is timed beside it for comparison.  Prints one JSON line."""
+    import mla_latent_kv_lat_amd as mla
+    from mla_inputs import OUT_FUSED_CONFIGS, OutProjInputs
+
+    c = OUT_FUSED_CONFIGS[name]
+    t0 = time.perf_counter()
+    inp = OutProjInputs(c["m"], c["heads"], c["d_model"], seed=c["seed"], d_v=c["d_v"])
+    M, H, dm, dv, dc = inp.m, inp.heads, inp.d_model, inp.d_v, inp.d_latent
+
+    def dev(u16):
+        return torch.from_numpy(np.ascontiguousarray(u16).view(np.int16)).view(torch.bfloat16).cuda()
+
+    o_lat, w_o, w_uv = dev(inp.o_lat), dev(inp.w_o), dev(inp.w_uv)
+    d = mla.dims(M, 1, H, 128, 64, dc, dv, mla.BF16, mla.BF16)
+    stream = torch.cuda.current_stream()
+    w_f = torch.empty((mla.mla_fused_out_weight_bytes(d, dm) // 2,), dtype=torch.bfloat16,
+                      device="cuda")
+    mla.mla_fuse_out_weight(d, dm, w_o, w_uv, w_f, stream)
+    ws = torch.empty(mla.mla_out_proj_fused_workspace_bytes(d, dm) // 4, dtype=torch.float32,
+                     device="cuda")
+    out = torch.empty((M, dm), dtype=torch.bfloat16, device="cuda")
+    # the unfused path's W_O product: o [M, H d_v] (the W_UV outputs) times W_O^T
+    o_v = torch.randn((M, H * dv), dtype=torch.bfloat16, device="cuda")
+    w_o_t = w_o.t().contiguous()
+    out_u = torch.empty((M, dm), dtype=torch.bfloat16, device="cuda")
+    torch.cuda.synchronize()
+    log(f"[bench] inputs for {name} ready in {time.perf_counter() - t0:.1f} s")
+
+    def fused():
+        mla.mla_out_proj_fused(d, dm, o_lat, w_f, ws, out, stream)
+
+    def unfused():
+        torch.mm(o_v, w_o_t, out=out_u)
+
+    for _ in range(args.warmup):
+        fused()
+        unfused()
+    torch.cuda.synchronize()
+    t_settle = time.perf_counter()
+    settle_steps = 0
+    while (time.perf_counter() - t_settle) * 1e3 < args.settle_ms:
+        for _ in range(10):
+            fused()
+            settle_steps += 1
+        torch.cuda.synchronize()
+    settle_ms = (time.perf_counter() - t_settle) * 1e3
+    if not torch.isfinite(out.float()).all():
+        raise RuntimeError("non-finite fused output projection")
+
+    def timed(fn):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for a, b in ev:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return np.array([a.elapsed_time(b) for a, b in ev])
+
+    f_ms = timed(fused)
+    u_ms = timed(unfused)
+    ms = float(np.median(f_ms))
+    w_bytes = dm * H * dc * 2
+    nbytes = w_bytes + M * H * dc * 2 + M * dm * 2
+    flops = 2.0 * M * dm * H * dc
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    u_bytes = dm * H * dv * 2 + M * H * dv * 2 + M * dm * 2
+    u_us = float(np.median(u_ms)) * 1e3
+    out_line = {
+        "metric": f"MLA fused output projection GB/s (pre-fused W_O W_UV, {H} heads, hidden {dm}, "
+                  f"{M} query tokens)",
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "us_per_step": round(ms * 1e3, 2),
+        "settle_ms": round(settle_ms, 1),
+        "settle_steps": settle_steps,
+        "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": name, "query_tokens": M, "heads": H, "d_latent": dc, "d_v": dv,
+                   "d_model": dm, "fused_weight_MB": round(w_bytes / 1e6, 1),
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                     "kernel": "out_fused_kernel + out_sum_kernel", "launch_us": round(ms * 1e3, 2),
+                     "timing": "median of events around each call (both kernels), on its stream"},
+        "unfused_w_o_gemm": {"us": round(u_us, 2), "bytes": u_bytes,
+                             "achieved_gbs": round(u_bytes / (u_us * 1e-6) / 1e9, 1),
+                             "what": "torch.mm of the W_UV outputs [M, H d_v] by W_O^T (the unfused "
+                                     "path's second product; its W_UV product is part of the fused "
+                                     "combine kernel)"},
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a sample ...")
+        out_line["cpu_baseline"] = out_fused_cpu_baseline(inp, nbytes, args.cpu_seconds)
+    print(json.dumps(out_line), flush=True)
+
+
+def out_fused_cpu_baseline(inp, nbytes: int, seconds: float):
+    """The float64 oracle's fused projection (out_proj_fused) for a sample of
+    output features: their fused-weight rows come from the oracle's
+    fuse_out_weight (load time, untimed).  value = the sample's share of the
+    call's bytes per second."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import bf16_to_f64, fuse_out_weight, out_proj_fused
+
+    rng = np.random.default_rng(2)
+    o = bf16_to_f64(inp.o_lat)
+    w_uv = bf16_to_f64(inp.w_uv)
+
+    def sample(k):
+        ns = rng.choice(inp.d_model, k, replace=False)
+        wf = fuse_out_weight(bf16_to_f64(inp.w_o[ns]), w_uv, inp.heads)
+        t1 = time.perf_counter()
+        out_proj_fused(o, wf)
+        return time.perf_counter() - t1
+
+    # at most 1024 features: their fused rows alone are 0.5 GB of float64
+    per = max(sample(16) / 16, 1e-5)
+    n = int(max(16, min(inp.d_model, 1024, seconds / per)))
+    dt = sample(n)
+    blas = max([t.get("num_threads", 1) for t in threadpool_info()] or [1])
+    cores = len(os.sched_getaffinity(0))
+    return {"value": round(n / inp.d_model * nbytes / dt / 1e9, 4), "unit": "GB/s",
+            "cores": int(min(blas, cores)), "host_cpus": cores, "os_cpu_count": os.cpu_count(),
+            "blas_threads": int(blas), "kind": "oracle",
+            "sample": f"{n} of {inp.d_model} output features for all {inp.m} query tokens, "
+                      f"{dt:.2f} s; value = the sample's share of the call's bytes / time"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -376,12 +522,15 @@ def main():
         return
 
     import mla_latent_kv_lat_amd as mla
-    from mla_inputs import CONFIGS, HEADLINE, PREFILL_CONFIGS, MLAInputs
+    from mla_inputs import CONFIGS, HEADLINE, OUT_FUSED_CONFIGS, PREFILL_CONFIGS, MLAInputs
     from mla_inputs.device import to_device
 
     name = args.workload or HEADLINE
     if name in PREFILL_CONFIGS:
         prefill_main(args, name, torch)
+        return
+    if name in OUT_FUSED_CONFIGS:
+        out_fused_main(args, name, torch)
         return
     cfg = CONFIGS[name]
     t0 = time.perf_counter()

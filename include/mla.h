@@ -379,31 +379,41 @@ int mla_prefill_attn(const mla_dims_t* dims, const void* q_nope, const void* q_r
  * returns MLA_ERR_UNSUPPORTED.  kv_dtype is not used.
  */
 
+/* Bytes of the fused weight mla_fuse_out_weight writes:
+ * ceil(d_model / 32) * 32 * H * d_latent * 2. */
+int mla_fused_out_weight_bytes(const mla_dims_t* dims, int32_t d_model, int64_t* bytes);
+
 /*
  * mla_fuse_out_weight -- the fused weight, once per layer (load time).
  *
  *   w_o      [d_model, H * d_v]   bf16, columns i*d_v .. i*d_v+d_v-1 are W_O,i
  *   w_uv     [H, d_v, d_latent]   bf16 (as in mla_out_proj)
- *   w_fused  [d_model, H, d_latent] bf16, output:
- *            w_fused[n, i, c] = sum_j w_o[n, i*d_v + j] * w_uv[i, j, c]
- *            (fp32 accumulate, one rounding to bf16)
+ *   w_fused  mla_fused_out_weight_bytes() bytes, output: the values
+ *            W~[n, k] = sum_j w_o[n, i*d_v + j] * w_uv[i, j, c],  k = i*d_latent + c
+ *            (fp32 accumulate, one rounding to bf16), stored in 1 KB blocks
+ *            in the order mla_out_proj_fused's matrix instructions read
+ *            them: with K = H * d_latent, element (n, k) sits at bf16 index
+ *              ((n/32 * K/16 + k/16) * 64 + ((k/8) % 2) * 32 + n % 32) * 8 + k % 8
+ *            and rows n from d_model to the next multiple of 32 are zero.
  */
 int mla_fuse_out_weight(const mla_dims_t* dims, int32_t d_model, const void* w_o,
                         const void* w_uv, void* w_fused, void* stream);
 
-/* Bytes of the fp32 workspace mla_out_proj_fused needs: 8 * batch * q_len
- * * d_model * 4 (partial sums of eight slices of the H * d_latent inputs). */
+/* Bytes of the workspace mla_out_proj_fused needs, with M = batch * q_len:
+ * 8 * M * d_model * 4 (fp32 partial sums of eight slices of the H * d_latent
+ * inputs) + ceil(M / 32) * 32 * H * d_latent * 2 (o_lat repacked into the
+ * order the matrix instructions read it). */
 int mla_out_proj_fused_workspace_bytes(const mla_dims_t* dims, int32_t d_model, int64_t* bytes);
 
 /*
  * mla_out_proj_fused -- the block output from the latent attention output.
  *
  *   o_lat     [B, Lq, H, d_latent] bf16 (mla_combine's o_lat)
- *   w_fused   [d_model, H, d_latent] bf16 (mla_fuse_out_weight's output)
+ *   w_fused   mla_fuse_out_weight's output for the same dims and d_model
  *   workspace mla_out_proj_fused_workspace_bytes() bytes, 16-byte aligned;
  *             overwritten (no initial contents needed)
  *   out       [B, Lq, d_model] bf16, output:
- *             out[b, t, n] = sum_{i, c} w_fused[n, i, c] * o_lat[b, t, i, c]
+ *             out[b, t, n] = sum_{i, c} W~[n, i*d_latent + c] * o_lat[b, t, i, c]
  *             (fp32 accumulate; the eight slice sums are added in a fixed
  *             order, so results repeat bit for bit)
  * batch == 0 returns MLA_OK with nothing enqueued.

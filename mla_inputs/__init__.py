@@ -7,7 +7,8 @@ the attention arithmetic: no RoPE, no projection, no softmax.  Both the CPU
 oracle and the GPU path consume what it produces.
 """
 
-from .configs import BLOCK_TOKENS, CONFIGS, HEADLINE, PREFILL_CONFIGS, MLAConfig, scaled
+from .configs import (BLOCK_TOKENS, CONFIGS, HEADLINE, OUT_FUSED_CONFIGS, PREFILL_CONFIGS, MLAConfig,
+                      scaled)
 from .generate import AppendInputs, MLAInputs, OutProjInputs, Pool
 
 __all__ = [
@@ -17,6 +18,7 @@ __all__ = [
     "HEADLINE",
     "MLAConfig",
     "MLAInputs",
+    "OUT_FUSED_CONFIGS",
     "OutProjInputs",
     "PREFILL_CONFIGS",
     "Pool",

@@ -124,3 +124,11 @@ PREFILL_CONFIGS = {
         name="prefill_b4_s4k", batch=4, q_len=4096, seq_len=4096, paged=True,
         causal=True, query_in_cache=True, seed=20261210, **_DSV3),
 }
+
+# Output-side absorption: the latent outputs of one decode step's query
+# tokens projected through the pre-fused W_O W_UV to the DeepSeek-V3 hidden
+# width 7168 (batch 64 with one or two query tokens per sequence).
+OUT_FUSED_CONFIGS = {
+    "out_fused_dsv3_m64": dict(m=64, heads=128, d_model=7168, d_v=128, seed=20261470),
+    "out_fused_dsv3_m128": dict(m=128, heads=128, d_model=7168, d_v=128, seed=20261471),
+}

@@ -75,6 +75,7 @@ def _load():
                              VP, VP],
         "mla_fuse_out_weight": [P, I32, VP, VP, VP, VP],
         "mla_out_proj_fused_workspace_bytes": [P, I32, ctypes.POINTER(I64)],
+        "mla_fused_out_weight_bytes": [P, I32, ctypes.POINTER(I64)],
         "mla_out_proj_fused": [P, I32, VP, VP, VP, VP, VP],
     }
     for name, args in sig.items():
@@ -249,6 +250,13 @@ def mla_fuse_out_weight(d: MLADims, d_model, w_o, w_uv, w_fused, stream=None):
     _check(_lib.mla_fuse_out_weight(ctypes.byref(d), int(d_model), _ptr(w_o), _ptr(w_uv),
                                     _ptr(w_fused), _stream(stream)),
            "mla_fuse_out_weight")
+
+
+def mla_fused_out_weight_bytes(d: MLADims, d_model) -> int:
+    out = ctypes.c_int64()
+    _check(_lib.mla_fused_out_weight_bytes(ctypes.byref(d), int(d_model), ctypes.byref(out)),
+           "mla_fused_out_weight_bytes")
+    return out.value
 
 
 def mla_out_proj_fused_workspace_bytes(d: MLADims, d_model) -> int:

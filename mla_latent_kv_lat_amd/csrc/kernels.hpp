@@ -85,7 +85,8 @@ hipError_t launch_out_proj_mfma(const mla_dims_t& d, const void* o_lat, const vo
 bool out_fused_supports(const mla_dims_t& d, int d_model);
 hipError_t launch_fuse_out(const mla_dims_t& d, int d_model, const void* w_o, const void* w_uv,
                            void* w_fused, hipStream_t s);
-int64_t out_fused_workspace_floats(const mla_dims_t& d, int d_model);
+int64_t fused_out_weight_elems(const mla_dims_t& d, int d_model);
+int64_t out_fused_workspace_bytes(const mla_dims_t& d, int d_model);
 hipError_t launch_out_fused(const mla_dims_t& d, int d_model, const void* o_lat, const void* w_fused,
                             float* workspace, void* out, hipStream_t s);
 

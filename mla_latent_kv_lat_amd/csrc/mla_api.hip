@@ -348,12 +348,21 @@ int mla_fuse_out_weight(const mla_dims_t* dims, int32_t d_model, const void* w_o
   return launched(launch_fuse_out(*dims, d_model, w_o, w_uv, w_fused, (hipStream_t)stream));
 }
 
+int mla_fused_out_weight_bytes(const mla_dims_t* dims, int32_t d_model, int64_t* bytes) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (d_model < 1 || !bytes) return MLA_ERR_INVALID_ARG;
+  if (!out_fused_supports(*dims, d_model)) return MLA_ERR_UNSUPPORTED;
+  *bytes = fused_out_weight_elems(*dims, d_model) * 2;
+  return MLA_OK;
+}
+
 int mla_out_proj_fused_workspace_bytes(const mla_dims_t* dims, int32_t d_model, int64_t* bytes) {
   int st = check_dims(dims);
   if (st) return st;
   if (d_model < 1 || !bytes) return MLA_ERR_INVALID_ARG;
   if (!out_fused_supports(*dims, d_model)) return MLA_ERR_UNSUPPORTED;
-  *bytes = out_fused_workspace_floats(*dims, d_model) * 4;
+  *bytes = out_fused_workspace_bytes(*dims, d_model);
   return MLA_OK;
 }
 

@@ -17,12 +17,18 @@
 // fuse_out_kernel (load time): W~[n][i][c] = sum_j W_O[n][i d_v + j] W_UV[i][j][c],
 //   one d x d_v by d_v x d_c product per head.  Not on the decode path: a
 //   plain LDS-tiled fp32 SIMT product, 64 x 64 outputs per workgroup with
-//   the whole K = d_v staged, rounded to bf16 once.
+//   the whole K = d_v staged, rounded to bf16 once.  It writes the weight in
+//   the order the projection's MFMAs consume it: 1 KB blocks of 32 features
+//   x 16 consecutive k, 16 bytes per lane, so that every load of the
+//   projection is one contiguous 1 KB and each wave streams a contiguous
+//   range (rows of a plain [d, H d_c] layout are 2 H d_c bytes apart, and
+//   32 of them per load instruction spread the stream thinly over memory).
 //
 // out_fused_kernel + out_sum_kernel (decode): u[m][n] = sum_k o~[m][k] W~[n][k]
 //   over k = (i, c), K = H d_c, for the M = B Lq query tokens.  Both operands
 //   are K-contiguous rows, so the 32x32x16 bf16 MFMA operands come straight
-//   from global memory (lane l: row l%32, 8 consecutive k).  The kernel
+//   from global memory (lane l: row l%32, 8 consecutive k; the weight's
+//   from its packed blocks, read non-temporally).  The kernel
 //   streams the fused weight, H x d x d_c bf16 (940 MB at H = 128,
 //   d = 7168), once per 128 query rows; at decode sizes it is bound by that
 //   stream.
@@ -72,92 +78,154 @@ __global__ __launch_bounds__(256) void fuse_out_kernel(const uint16_t* __restric
 #pragma unroll
       for (int q = 0; q < 4; ++q) acc[r][q] = fmaf(a[r], b[q], acc[r][q]);
   }
+  // packed store: element (n, k = i d_c + c) of the [d, H d_c] product goes to
+  // 1 KB block (n / 32, k / 16), lane 32 ((k % 16) / 8) + n % 32, slot k % 8;
+  // rows from d_model up to the next multiple of 32 are zero
+  const int64_t ksteps = (int64_t)H * d_c / 16;
+  const int npad = (d_model + 31) & ~31;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int n = n0 + 4 * ty + r;
-    if (n >= d_model) continue;
+    if (n >= npad) continue;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int c = c0 + 4 * tx + q;
-      if (c < d_c) w_f[((int64_t)n * H + i) * d_c + c] = f32_to_bf16(acc[r][q]);
+      if (c >= d_c) continue;
+      const int64_t k = (int64_t)i * d_c + c;
+      const int64_t off = (((int64_t)(n >> 5) * ksteps + (k >> 4)) * 64 + ((k >> 3) & 1) * 32 +
+                           (n & 31)) * 8 + (k & 7);
+      w_f[off] = n < d_model ? f32_to_bf16(acc[r][q]) : (uint16_t)0;
     }
   }
 }
 
-// K = H d_c is cut into kOfSplit chunks, one per XCD (workgroup id mod 8 is
-// the XCD the dispatcher places it on), so a chunk's rows of o~ are fetched
-// into that XCD's L2 once and shared by its workgroups.  Each workgroup
-// owns 128 output features (32 per wave) of one chunk and writes fp32
-// partial sums; out_sum_kernel adds the chunks in a fixed order.
 constexpr int kOfSplit = 8;
 
-// RT row tiles of 32 query rows per pass, PF k-steps of loads in flight.
-template <int RT, int PF>
-__global__ __launch_bounds__(256) void out_fused_kernel(const uint16_t* __restrict__ o_lat,
+// A workgroup (4 waves) owns 64 FT features of one chunk: wave w takes the
+// FT 32-feature blocks of group w & 1 and half w >> 1 of the chunk's k-steps
+// (the halves are added through LDS), RT row tiles of 32 query rows per
+// pass and PF k-steps of loads in flight.  Each k-step loads RT tiles of o~
+// and FT blocks of the weight for RT x FT MFMAs.
+template <int RT, int FT, int PF>
+__global__ __launch_bounds__(256, 2) void out_fused_kernel(const uint16_t* __restrict__ a_pk,
                                                         const uint16_t* __restrict__ w_f,
                                                         float* __restrict__ part, int M,
                                                         int d_model, int K) {
+  static_assert(RT * FT <= 8, "LDS holds eight accumulators per lane");
+  __shared__ f32x16 red[2][8][64];  // half 1's accumulators, per feature group
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int fg = w & 1, kh = w >> 1;
   const int chunk = blockIdx.x & (kOfSplit - 1);
-  const int n0 = (blockIdx.x / kOfSplit) * 128 + 32 * w;
+  const int nbase = (blockIdx.x / kOfSplit) * 2 * FT + fg * FT;  // first 32-feature block
+  const int nblocks = (d_model + 31) >> 5;
   const int l32 = lane & 31, hk = lane >> 5;
-  // features past the end re-read the last row (their results are not stored)
-  const int n = min(n0 + l32, d_model - 1);
-  const int kc = K / kOfSplit;  // a multiple of 16 (K = 512 H)
-  const int steps = kc >> 4;
-  // k-step s of the chunk: elements chunk kc + 16 s + 8 hk .. +7, i.e. the
-  // 8-element unit kb + 2 s of a K-contiguous row
-  const int kb = chunk * (kc >> 3) + hk;
-  const bf16x8* brow = (const bf16x8*)(w_f + (int64_t)n * K) + kb;
+  const int kc = K / kOfSplit;  // a multiple of 64 (K = 512 H)
+  const int steps = kc >> 5;    // per half
+  // k-step s of this half is k-step chunk kc/16 + kh steps + s of K; both
+  // operands are packed in 1 KB blocks per (32-row tile, k-step), lane l's
+  // 16 bytes holding row l%32, k 16 s + 8 (l/32) .. +7
+  const int64_t sbase = (int64_t)chunk * (kc >> 4) + kh * steps;
+  const int ntiles = (M + 31) >> 5;
+  const bf16x8* brow[FT];
+#pragma unroll
+  for (int f = 0; f < FT; ++f) {
+    // blocks past the last (their results are not stored) re-read the last one
+    const int nbl = min(nbase + f, nblocks - 1);
+    brow[f] = (const bf16x8*)w_f + ((int64_t)nbl * (K >> 4) + sbase) * 64 + lane;
+  }
   float* pout = part + (int64_t)chunk * M * d_model;
   for (int mg = blockIdx.y * 32 * RT; mg < M; mg += gridDim.y * 32 * RT) {
     const bf16x8* arow[RT];
 #pragma unroll
-    for (int t = 0; t < RT; ++t)
-      arow[t] = (const bf16x8*)(o_lat + (int64_t)min(mg + 32 * t + l32, M - 1) * K) + kb;
-    bf16x8 a[PF][RT], b[PF];
+    for (int t = 0; t < RT; ++t) {
+      // tiles past the last (their results are not stored) re-read the last one
+      const int tile = min((mg >> 5) + t, ntiles - 1);
+      arow[t] = (const bf16x8*)a_pk + ((int64_t)tile * (K >> 4) + sbase) * 64 + lane;
+    }
+    bf16x8 a[PF][RT], b[PF][FT];
 #pragma unroll
     for (int d = 0; d < PF; ++d) {
       if (d < steps) {
-        b[d] = brow[2 * d];
 #pragma unroll
-        for (int t = 0; t < RT; ++t) a[d][t] = arow[t][2 * d];
+        for (int f = 0; f < FT; ++f) b[d][f] = __builtin_nontemporal_load(brow[f] + 64 * d);
+#pragma unroll
+        for (int t = 0; t < RT; ++t) a[d][t] = arow[t][64 * d];
       }
     }
-    f32x16 acc[RT];
+    f32x16 acc[RT][FT];
 #pragma unroll
-    for (int t = 0; t < RT; ++t) acc[t] = f32x16{};
+    for (int t = 0; t < RT; ++t)
+#pragma unroll
+      for (int f = 0; f < FT; ++f) acc[t][f] = f32x16{};
     for (int s0 = 0; s0 < steps; s0 += PF) {
 #pragma unroll
       for (int d = 0; d < PF; ++d) {
         if (s0 + d < steps) {
-          const bf16x8 bv = b[d];
-          bf16x8 av[RT];
+          bf16x8 av[RT], bv[FT];
 #pragma unroll
           for (int t = 0; t < RT; ++t) av[t] = a[d][t];
+#pragma unroll
+          for (int f = 0; f < FT; ++f) bv[f] = b[d][f];
           const int sn = s0 + d + PF;
           if (sn < steps) {
-            b[d] = brow[2 * sn];
 #pragma unroll
-            for (int t = 0; t < RT; ++t) a[d][t] = arow[t][2 * sn];
+            for (int f = 0; f < FT; ++f) b[d][f] = __builtin_nontemporal_load(brow[f] + 64 * sn);
+#pragma unroll
+            for (int t = 0; t < RT; ++t) a[d][t] = arow[t][64 * sn];
           }
 #pragma unroll
-          for (int t = 0; t < RT; ++t) acc[t] = mfma32(av[t], bv, acc[t]);
+          for (int t = 0; t < RT; ++t)
+#pragma unroll
+            for (int f = 0; f < FT; ++f) acc[t][f] = mfma32(av[t], bv[f], acc[t][f]);
         }
       }
     }
-    // D (32 x 32) of row tile t: lane l holds feature n0 + l%32 and rows
-    // mg + 32 t + 8(r/4) + 4(l/32) + r%4
-    if (n0 + l32 < d_model) {
+    if (kh == 1) {
 #pragma unroll
       for (int t = 0; t < RT; ++t)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int m = mg + 32 * t + 8 * (r >> 2) + 4 * hk + (r & 3);
-          if (m < M) pout[(int64_t)m * d_model + n0 + l32] = acc[t][r];
+        for (int f = 0; f < FT; ++f) red[fg][t * FT + f][lane] = acc[t][f];
+    }
+    __syncthreads();
+    if (kh == 0) {
+      // D (32 x 32) of (row tile t, block f): lane l holds feature
+      // 32 (nbase + f) + l%32 and rows mg + 32 t + 8(r/4) + 4(l/32) + r%4
+#pragma unroll
+      for (int t = 0; t < RT; ++t)
+#pragma unroll
+        for (int f = 0; f < FT; ++f) {
+          const f32x16 v = acc[t][f] + red[fg][t * FT + f][lane];
+          const int n = 32 * (nbase + f) + l32;
+          if (n >= d_model) continue;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int m = mg + 32 * t + 8 * (r >> 2) + 4 * hk + (r & 3);
+            if (m < M) pout[(int64_t)m * d_model + n] = v[r];
+          }
         }
     }
+    __syncthreads();  // red is free for the next pass
+  }
+}
+
+// o~ [M, K] into the operand blocks out_fused_kernel reads: 16-byte unit
+// (tile, s, l) holds row 32 tile + l%32, k 16 s + 8 (l/32) .. +7; rows from
+// M up to the next multiple of 32 are zero.
+__global__ __launch_bounds__(256) void pack_rows_kernel(const uint16_t* __restrict__ o_lat,
+                                                        bf16x8* __restrict__ a_pk, int M, int K,
+                                                        int64_t units) {
+  const int ks = K >> 4;
+  for (int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x; u < units;
+       u += (int64_t)gridDim.x * 256) {
+    const int l = (int)(u & 63);
+    const int64_t ts = u >> 6;
+    const int64_t tile = ts / ks;
+    const int st = (int)(ts - tile * ks);
+    const int64_t m = tile * 32 + (l & 31);
+    bf16x8 v = bf16x8{};
+    if (m < M) v = *(const bf16x8*)(o_lat + m * K + 16 * st + 8 * (l >> 5));
+    a_pk[u] = v;
   }
 }
 
@@ -189,26 +257,43 @@ hipError_t launch_fuse_out(const mla_dims_t& d, int d_model, const void* w_o, co
   return hipGetLastError();
 }
 
-int64_t out_fused_workspace_floats(const mla_dims_t& d, int d_model) {
-  return (int64_t)kOfSplit * d.batch * d.q_len * d_model;
+int64_t fused_out_weight_elems(const mla_dims_t& d, int d_model) {
+  return (int64_t)((d_model + 31) / 32) * 32 * d.heads * d.d_latent;
+}
+
+// workspace: kOfSplit partial sums [M, d] (fp32), then the packed o~
+// (ceil(M/32) 32 x K bf16)
+int64_t out_fused_workspace_bytes(const mla_dims_t& d, int d_model) {
+  const int64_t M = (int64_t)d.batch * d.q_len;
+  return (int64_t)kOfSplit * M * d_model * 4 + (M + 31) / 32 * 32 * d.heads * d.d_latent * 2;
 }
 
 hipError_t launch_out_fused(const mla_dims_t& d, int d_model, const void* o_lat, const void* w_fused,
                             float* workspace, void* out, hipStream_t s) {
   const int M = d.batch * d.q_len, K = d.heads * d.d_latent;
   if (M == 0) return hipSuccess;
-  const unsigned gx = (unsigned)(((d_model + 127) / 128) * kOfSplit);
+  const int nblocks = (d_model + 31) / 32;
+  bf16x8* apk = (bf16x8*)(workspace + (int64_t)kOfSplit * M * d_model);
+  const int64_t units = (int64_t)(M + 31) / 32 * 32 * K / 8;
+  const unsigned gp = (unsigned)((units + 255) / 256 < 2048 ? (units + 255) / 256 : 2048);
+  hipLaunchKernelGGL(pack_rows_kernel, dim3(gp), dim3(256), 0, s, (const uint16_t*)o_lat, apk, M, K,
+                     units);
+  const uint16_t* a = (const uint16_t*)apk;
+  const uint16_t* w = (const uint16_t*)w_fused;
   if (M <= 32) {
-    hipLaunchKernelGGL((out_fused_kernel<1, 8>), dim3(gx), dim3(256), 0, s, (const uint16_t*)o_lat,
-                       (const uint16_t*)w_fused, workspace, M, d_model, K);
+    const unsigned gx = (unsigned)((nblocks + 3) / 4 * kOfSplit);
+    hipLaunchKernelGGL((out_fused_kernel<1, 2, 4>), dim3(gx), dim3(256), 0, s, a, w, workspace, M,
+                       d_model, K);
   } else if (M <= 64) {
-    hipLaunchKernelGGL((out_fused_kernel<2, 8>), dim3(gx), dim3(256), 0, s, (const uint16_t*)o_lat,
-                       (const uint16_t*)w_fused, workspace, M, d_model, K);
+    const unsigned gx = (unsigned)((nblocks + 3) / 4 * kOfSplit);
+    hipLaunchKernelGGL((out_fused_kernel<2, 2, 4>), dim3(gx), dim3(256), 0, s, a, w, workspace, M,
+                       d_model, K);
   } else {
     // 128 rows per pass; passes beyond the grid's rows loop inside
+    const unsigned gx = (unsigned)((nblocks + 3) / 4 * kOfSplit);
     const unsigned gy = (unsigned)min((M + 127) / 128, 65535);
-    hipLaunchKernelGGL((out_fused_kernel<4, 4>), dim3(gx, gy), dim3(256), 0, s,
-                       (const uint16_t*)o_lat, (const uint16_t*)w_fused, workspace, M, d_model, K);
+    hipLaunchKernelGGL((out_fused_kernel<4, 2, 2>), dim3(gx, gy), dim3(256), 0, s, a, w, workspace,
+                       M, d_model, K);
   }
   const int64_t total = (int64_t)M * d_model;
   const unsigned gs = (unsigned)((total + 255) / 256 < 4096 ? (total + 255) / 256 : 4096);

@@ -284,5 +284,8 @@ def test_out_fused_validation():
     assert proj(_d(batch=1 << 20)) == 2                          # rows x d_model past 2^31
     n = ctypes.c_int64()
     assert lib.mla_out_proj_fused_workspace_bytes(ctypes.byref(d), 7168, ctypes.byref(n)) == 0
-    assert n.value == 8 * 64 * 7168 * 4
-    assert mla.mla_out_proj_fused_workspace_bytes(_d(batch=3, q_len=2), 100) == 8 * 6 * 100 * 4
+    assert n.value == 8 * 64 * 7168 * 4 + 64 * 128 * 512 * 2
+    assert mla.mla_out_proj_fused_workspace_bytes(_d(batch=3, q_len=2), 100) == \
+        8 * 6 * 100 * 4 + 32 * 128 * 512 * 2
+    assert mla.mla_fused_out_weight_bytes(_d(batch=3), 100) == 128 * 128 * 512 * 2  # rows to 128
+    assert mla.mla_fused_out_weight_bytes(_d(batch=3, heads=2), 7168) == 7168 * 2 * 512 * 2

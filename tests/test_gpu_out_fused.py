@@ -43,15 +43,27 @@ def run_fused(inp, tensors=None):
     d = _dims(inp)
     t = tensors or {"o_lat": _dev(inp.o_lat), "w_o": _dev(inp.w_o), "w_uv": _dev(inp.w_uv)}
     H, dc = inp.heads, inp.d_latent
-    w_f = torch.full((inp.d_model, H, dc), float("nan"), dtype=torch.bfloat16, device="cuda")
+    w_f = torch.full((mla.mla_fused_out_weight_bytes(d, inp.d_model) // 2,), float("nan"),
+                     dtype=torch.bfloat16, device="cuda")
     out = torch.full((inp.m, inp.d_model), float("nan"), dtype=torch.bfloat16, device="cuda")
-    ws = torch.empty(mla.mla_out_proj_fused_workspace_bytes(d, inp.d_model) // 4 + 4,
+    ws = torch.empty(mla.mla_out_proj_fused_workspace_bytes(d, inp.d_model) // 4,
                      dtype=torch.float32, device="cuda")
     ws.fill_(float("nan"))  # no initial contents are needed
     mla.mla_fuse_out_weight(d, inp.d_model, t["w_o"], t["w_uv"], w_f)
     mla.mla_out_proj_fused(d, inp.d_model, t["o_lat"], w_f, ws, out)
     torch.cuda.synchronize()
     return w_f, out, t
+
+
+def fused_rows(inp, w_f, ns):
+    """Rows ns of the fused weight, [len(ns), H, d_c], gathered from its
+    packed 1 KB blocks (element (n, k) at ((n/32 K/16 + k/16) 64 +
+    ((k/8) % 2) 32 + n % 32) 8 + k % 8)."""
+    K = inp.heads * inp.d_latent
+    w5 = w_f.view(-1, K // 16, 2, 32, 8)
+    nb = torch.from_numpy(np.asarray(ns) // 32).cuda()
+    r = torch.from_numpy(np.asarray(ns) % 32).cuda()
+    return w5[nb, :, :, r, :].reshape(len(ns), inp.heads, inp.d_latent)
 
 
 def check(inp, w_f, out, rows=None, label=""):
@@ -61,7 +73,10 @@ def check(inp, w_f, out, rows=None, label=""):
     ns = np.arange(inp.d_model) if rows is None else np.asarray(rows)
     w_ref = fuse_out_weight(bf16_to_f64(inp.w_o[ns]), bf16_to_f64(inp.w_uv), H)
     idx = torch.from_numpy(ns).cuda()
-    w_got = _np(w_f[idx])
+    w_got = _np(fused_rows(inp, w_f, ns))
+    pad = np.arange(inp.d_model, -(-inp.d_model // 32) * 32)
+    if len(pad):
+        assert not fused_rows(inp, w_f, pad).float().abs().sum().item(), "padding rows not zero"
     err_w = row_rel_err(w_got.reshape(len(ns) * H, -1), w_ref.reshape(len(ns) * H, -1))
     o_ref = out_proj_fused(bf16_to_f64(inp.o_lat), w_ref)
     o_got = _np(out[:, idx])
