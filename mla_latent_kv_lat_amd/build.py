@@ -54,6 +54,7 @@ DECODE_SOURCES = ("decode_split.hip", "decode_common.hpp", "mfma_common.hpp", "c
                   "kernels.hpp")
 PREFILL_SOURCES = ("prefill.hip", "decode_common.hpp", "mfma_common.hpp", "common.hpp",
                    "kernels.hpp")
+OUT_FUSED_SOURCES = ("out_fused.hip", "mfma_common.hpp", "common.hpp", "kernels.hpp")
 
 
 def source_digest(files=None) -> str:
