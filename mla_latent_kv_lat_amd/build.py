@@ -59,10 +59,13 @@ OUT_FUSED_SOURCES = ("out_fused.hip", "mfma_common.hpp", "common.hpp", "kernels.
 
 def source_digest(files=None) -> str:
     """Hash of library sources and the header (ties measurements to code):
-    all sources, or only `files` (names under csrc/)."""
+    the library's build inputs (SOURCES and the headers under csrc/), or
+    only `files` (names under csrc/).  Other files lying in csrc/ do not
+    enter the library and do not change the hash."""
     import hashlib
     h = hashlib.sha256()
-    names = sorted(files) if files else sorted(f for f in os.listdir(CSRC) if f.endswith((".hip", ".hpp")))
+    names = sorted(files) if files else sorted(
+        set(SOURCES) | {f for f in os.listdir(CSRC) if f.endswith(".hpp")})
     for f in names:
         with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(f.encode() + b"\0" + fh.read())
