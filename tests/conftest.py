@@ -24,5 +24,5 @@ def pytest_terminal_summary(terminalreporter, exitstatus, config):
         frac = max(errs.values()) / tol if errs else 0.0
         worst = max(worst, frac)
         tr.write_line(f"{label}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items())
-                      + f" gate={tol:.0e} worst={frac:.2f}")
+                      + f" gate={tol:.2g} worst={frac:.2f}")
     tr.write_line(f"{len(RECORDED)} cases, largest error / gate = {worst:.2f}")
