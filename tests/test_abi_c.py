@@ -3,28 +3,22 @@ against include/mla.h and linked with libmla.so, calls the host-only entry
 points; its results must equal the Python binding's (same library)."""
 
 import os
-import shutil
 import subprocess
 
 import pytest
 
 import mla_latent_kv_lat_amd as mla
 from mla_latent_kv_lat_amd import binding
-
-ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+from tests._cprog import program
 
 
 @pytest.fixture(scope="module")
 def c_output(tmp_path_factory):
-    if shutil.which("gcc") is None:
-        pytest.skip("no C compiler")
-    lib_dir = os.path.dirname(binding.LIB_PATH)
     if not os.path.exists(binding.LIB_PATH):
         pytest.skip("library not built")
-    exe = str(tmp_path_factory.mktemp("abi_c") / "abi_c_check")
-    subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror",
-                    "-I", os.path.join(ROOT, "include"), os.path.join(ROOT, "tests", "abi_c_check.c"),
-                    "-L", lib_dir, "-lmla", f"-Wl,-rpath,{lib_dir}", "-o", exe], check=True)
+    exe = program("abi_c_check", str(tmp_path_factory.mktemp("abi_c")))
+    if exe is None:
+        pytest.skip("no C compiler")
     out = subprocess.run([exe], check=True, capture_output=True, text=True, timeout=60).stdout
     return [line.split() for line in out.splitlines()]
 

@@ -6,7 +6,6 @@ writes o and lse back.  They must match the float64 oracle at the bf16 gate
 and equal, bit for bit, the same step run through the Python binding."""
 
 import os
-import shutil
 import subprocess
 
 import numpy as np
@@ -14,28 +13,13 @@ import pytest
 import torch
 
 import mla_latent_kv_lat_amd as mla
-from mla_latent_kv_lat_amd import binding
 from mla_inputs import CONFIGS, MLAInputs, scaled
 from mla_inputs.device import to_device
 from oracle import mla_decode
+from tests._cprog import program
 from tests._metrics import record, row_rel_err, tol_for
 
 pytestmark = pytest.mark.gpu
-
-ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-
-
-def _build(tmp):
-    if shutil.which("gcc") is None:
-        pytest.skip("no C compiler")
-    lib_dir = os.path.dirname(binding.LIB_PATH)
-    exe = os.path.join(tmp, "abi_c_decode")
-    subprocess.run(["gcc", "-std=c11", "-Wall", "-Wextra", "-pedantic", "-Werror",
-                    "-D__HIP_PLATFORM_AMD__", "-isystem", "/opt/rocm/include",
-                    "-I", os.path.join(ROOT, "include"), os.path.join(ROOT, "tests", "abi_c_decode.c"),
-                    "-L", lib_dir, "-lmla", "-L", "/opt/rocm/lib", "-lamdhip64",
-                    f"-Wl,-rpath,{lib_dir}", "-Wl,-rpath,/opt/rocm/lib", "-o", exe], check=True)
-    return exe
 
 
 def _bf16(u16):
@@ -60,8 +44,10 @@ def test_decode_step_from_c(tmp_path, paged):
         f.write(f"{c.batch} {c.q_len} {c.heads} {c.d_nope} {c.d_rope} {c.d_latent} {c.d_v} "
                 f"{mla.BF16} {mla.BF16} {c.row_width} {pool.max_blocks_per_seq} {pool.max_seq_len} "
                 f"{int(c.causal)} {int(paged)} {inp.softmax_scale!r} {inp.rope_base!r}\n")
-    exe = _build(d)
-    print(f"[c abi] running the C decode step, paged={paged}", flush=True)
+    exe = program("abi_c_decode", d)
+    if exe is None:
+        pytest.skip("no C compiler")
+    print(f"[c abi] running the C decode step ({exe}), paged={paged}", flush=True)
     r = subprocess.run([exe, d], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0, r.stderr
     G = int(r.stdout.split()[1])
