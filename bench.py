@@ -528,7 +528,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures the one-GPU path only (asked for {max(args.gpus, world)} GPUs); "
-              "the decode step has no multi-GPU mode in this build.", file=sys.stderr)
+              "the library runs the decode step on a single GPU (no multi-GPU mode).", file=sys.stderr)
         sys.exit(2)
 
     import torch
